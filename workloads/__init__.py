@@ -1,0 +1,261 @@
+"""Seeded synthetic workloads for closed-form tree verification of Gated DeltaNet layers.
+
+This module only draws random numbers and rounds them to the storage types the
+library consumes.  It holds none of the method's arithmetic: no recurrence, no
+gate products, no factors.  Both the CPU oracle (``oracle/``) and the HIP
+library read their inputs from here, so the two see exactly the same bits.
+
+Workload shapes follow the five verification settings studied on the pages
+(Bole, arXiv 2608.01651: single-request decode, batched verify, ragged forests,
+a multi-layer round) plus the B=16/T=64 headline shape.  Trees are random
+recursive trees with a depth cap, which stand in for the drafter-built proposal
+trees of the paper's evaluation (no drafter or dataset is used).
+
+Value distributions (per node and head):
+  q, k ~ N(0, 1), then L2-normalised over the key dimension (in float64),
+  v ~ N(0, 1),
+  g = log(gamma) = -softplus(x) with x ~ N(mu_x, 1)  (mu_x = 0, or -3 for the
+      deep-chain stress setting so that gamma sits near 1),
+  beta = sigmoid(N(0, 1)).
+All values are generated in float64, then rounded to float32 (round to nearest
+even) and, for bf16 workloads, q/k/v further to bfloat16 (round to nearest even).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+# RNG stream ids (part of the SeedSequence entropy).
+STREAM_TOPOLOGY = 0
+STREAM_TOKENS = 1
+STREAM_PREFIX = 2
+STREAM_ACCEPT = 3
+
+MAX_TREE = 64  # one 64-bit ancestor mask per node
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    cid: int            # entropy id for the seed sequence
+    B: int              # requests (trees)
+    H: int              # state heads
+    d_k: int
+    d_v: int
+    dtype: str          # "f32" or "bf16" for q/k/v (gates and state are always f32)
+    tree: str           # "heap7" | "fixed" | "ragged"
+    T: int              # nodes per tree (fixed) or max size (ragged)
+    D: int              # depth cap: a new node's parent has depth < D
+    prefix: int         # prefix tokens used to build the committed state
+    L: int = 1          # GDN layers in the round
+    gate_mu: float = 0.0
+    T_min: int = 0      # ragged: smallest tree
+    N_cap: int = 0      # ragged: total node cap
+
+
+CONFIGS: Dict[str, Config] = {
+    # Exactness case: full binary tree of 7 nodes, float32 everything.
+    "tiny": Config("tiny", 1, B=1, H=1, d_k=16, d_v=16, dtype="f32", tree="heap7",
+                   T=7, D=2, prefix=32),
+    # Single-request decode shape.
+    "decode": Config("decode", 2, B=1, H=16, d_k=128, d_v=128, dtype="bf16",
+                     tree="fixed", T=8, D=4, prefix=256),
+    # Batched verify, 16 trees of 32 nodes.
+    "batched": Config("batched", 3, B=16, H=32, d_k=128, d_v=128, dtype="bf16",
+                      tree="fixed", T=32, D=8, prefix=256),
+    # Ragged forest, sizes 8..64, deep chains with gates near one.
+    "ragged": Config("ragged", 4, B=16, H=32, d_k=128, d_v=128, dtype="bf16",
+                     tree="ragged", T=64, D=16, prefix=256, gate_mu=-3.0,
+                     T_min=8, N_cap=768),
+    # Multi-layer round: 36 layers, 32 trees of 64 nodes.
+    "multilayer": Config("multilayer", 5, B=32, H=32, d_k=128, d_v=128, dtype="bf16",
+                         tree="fixed", T=64, D=12, prefix=256, L=36),
+    # Headline throughput shape: the multi-layer tree rule at 16 requests, one layer.
+    "target": Config("target", 6, B=16, H=32, d_k=128, d_v=128, dtype="bf16",
+                     tree="fixed", T=64, D=12, prefix=256),
+}
+
+
+def _rng(seed: int, cfg: Config, stream: int, *more: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, cfg.cid, stream, *more]))
+
+
+# ----------------------------------------------------------------------------
+# rounding helpers (storage formats only)
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest even); returns the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_storage(x: np.ndarray, dtype: str):
+    """float64 -> (storage array, float64 view of exactly the stored values)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return x32, x32.astype(np.float64)
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x32)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# topology
+
+def random_tree(rng: np.random.Generator, T: int, D: int) -> np.ndarray:
+    """Random recursive tree: node 0 is the root; node i picks its parent uniformly
+    among earlier nodes whose depth is below D.  Parents precede children."""
+    parent = np.full(T, -1, dtype=np.int32)
+    depth = np.zeros(T, dtype=np.int32)
+    for i in range(1, T):
+        cand = np.nonzero(depth[:i] < D)[0]
+        p = int(cand[rng.integers(len(cand))])
+        parent[i] = p
+        depth[i] = depth[p] + 1
+    return parent
+
+
+@dataclass
+class Forest:
+    parent: np.ndarray      # [N] int32, local parent index, -1 for the root
+    tree_off: np.ndarray    # [B+1] int32
+    accept: np.ndarray      # [B] int32, last accepted local node (-1 = none)
+
+    @property
+    def B(self) -> int:
+        return len(self.tree_off) - 1
+
+    @property
+    def N(self) -> int:
+        return int(self.tree_off[-1])
+
+    def sizes(self) -> np.ndarray:
+        return np.diff(self.tree_off)
+
+
+def make_forest(cfg: Config, seed: int = 0) -> Forest:
+    rng = _rng(seed, cfg, STREAM_TOPOLOGY)
+    if cfg.tree == "heap7":
+        trees = [np.array([-1, 0, 0, 1, 1, 2, 2], dtype=np.int32)] * cfg.B
+    elif cfg.tree == "fixed":
+        trees = [random_tree(rng, cfg.T, cfg.D) for _ in range(cfg.B)]
+    elif cfg.tree == "ragged":
+        while True:
+            sizes = rng.integers(cfg.T_min, cfg.T + 1, size=cfg.B)
+            if sizes.sum() <= cfg.N_cap:
+                break
+        trees = [random_tree(rng, int(t), cfg.D) for t in sizes]
+    else:
+        raise ValueError(cfg.tree)
+    off = np.zeros(cfg.B + 1, dtype=np.int32)
+    off[1:] = np.cumsum([len(t) for t in trees])
+    parent = np.concatenate(trees).astype(np.int32)
+    if cfg.tree == "heap7":
+        accept = np.full(cfg.B, 3, dtype=np.int32)  # root -> leftmost leaf
+    else:
+        arng = _rng(seed, cfg, STREAM_ACCEPT)
+        accept = np.array([arng.integers(len(t)) for t in trees], dtype=np.int32)
+    return Forest(parent=parent, tree_off=off, accept=accept)
+
+
+# ----------------------------------------------------------------------------
+# per-layer token operands
+
+def _unit_rows(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _gates(rng, shape, mu):
+    x = rng.standard_normal(shape) + mu
+    g = -(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x))))   # -softplus(x)
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+    return g, beta
+
+
+@dataclass
+class LayerInputs:
+    """Token operands of one GDN layer, token-major [N, H, d]."""
+    q: np.ndarray           # storage (float32 or uint16 bf16 bits)
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray           # [N, H] float32, log of the decay gate
+    beta: np.ndarray        # [N, H] float32
+    q64: np.ndarray         # float64 copies of exactly the stored values
+    k64: np.ndarray
+    v64: np.ndarray
+    dtype: str
+
+    @property
+    def g64(self):
+        return self.g.astype(np.float64)
+
+    @property
+    def beta64(self):
+        return self.beta.astype(np.float64)
+
+
+def make_layer(cfg: Config, N: int, layer: int = 0, seed: int = 0) -> LayerInputs:
+    rng = _rng(seed, cfg, STREAM_TOKENS, layer)
+    H = cfg.H
+    q = _unit_rows(rng, N * H, cfg.d_k).reshape(N, H, cfg.d_k)
+    k = _unit_rows(rng, N * H, cfg.d_k).reshape(N, H, cfg.d_k)
+    v = rng.standard_normal((N, H, cfg.d_v))
+    g, beta = _gates(rng, (N, H), cfg.gate_mu)
+    qs, q64 = round_storage(q, cfg.dtype)
+    ks, k64 = round_storage(k, cfg.dtype)
+    vs, v64 = round_storage(v, cfg.dtype)
+    return LayerInputs(q=qs, k=ks, v=vs, g=g.astype(np.float32),
+                       beta=beta.astype(np.float32), q64=q64, k64=k64, v64=v64,
+                       dtype=cfg.dtype)
+
+
+@dataclass
+class PrefixTokens:
+    """Committed-prefix tokens of one (layer, request, head) state, [P, d]."""
+    q64: np.ndarray
+    k64: np.ndarray
+    v64: np.ndarray
+    g64: np.ndarray
+    beta64: np.ndarray
+
+
+def make_prefix(cfg: Config, layer: int, b: int, h: int, seed: int = 0) -> PrefixTokens:
+    """Tokens that precede the tree for one state head.  The committed state the
+    tree starts from is the result of running the sequential recurrence over
+    them from a zero state (done by the caller)."""
+    rng = _rng(seed, cfg, STREAM_PREFIX, layer, b, h)
+    P = cfg.prefix
+    q = _unit_rows(rng, P, cfg.d_k)
+    k = _unit_rows(rng, P, cfg.d_k)
+    v = rng.standard_normal((P, cfg.d_v))
+    g, beta = _gates(rng, (P,), cfg.gate_mu)
+    return PrefixTokens(q64=round_storage(q, cfg.dtype)[1], k64=round_storage(k, cfg.dtype)[1],
+                        v64=round_storage(v, cfg.dtype)[1],
+                        g64=g.astype(np.float32).astype(np.float64),
+                        beta64=beta.astype(np.float32).astype(np.float64))
+
+
+def chain_forest(B: int, T: int) -> Forest:
+    """B chains of T nodes each (node i's parent is i-1)."""
+    one = np.arange(-1, T - 1, dtype=np.int32)
+    off = np.arange(0, (B + 1) * T, T, dtype=np.int32)
+    return Forest(parent=np.tile(one, B), tree_off=off,
+                  accept=np.full(B, T - 1, dtype=np.int32))
+
+
+def forest_from_trees(trees: List[np.ndarray], accept: Optional[List[int]] = None) -> Forest:
+    off = np.zeros(len(trees) + 1, dtype=np.int32)
+    off[1:] = np.cumsum([len(t) for t in trees])
+    acc = np.array(accept if accept is not None else [len(t) - 1 for t in trees], dtype=np.int32)
+    return Forest(parent=np.concatenate(trees).astype(np.int32), tree_off=off, accept=acc)
