@@ -1,0 +1,187 @@
+/*
+ * bole.h - C ABI of libbole.so: closed-form tree verification for Gated DeltaNet
+ * (GDN) layers on AMD MI355X (gfx950).
+ *
+ * The method is Bole (arXiv 2608.01651, "Bole: Efficient Tree Speculation for
+ * Hybrid-Attention Language Models").  For every node of a speculative proposal
+ * tree it computes, from one immutable pre-tree state S_pre (Theorem 1, Eq. 2):
+ *
+ *     O = D_P Q S_pre + C (I + G)^{-1} D_beta (V - D_P K S_pre)
+ *
+ * with P_i the product of decay gates over node i's root-to-node path (i
+ * included), G_ij = beta_i (P_i/P_j) k_i.k_j over strict ancestors j (Lemma 2,
+ * Eq. 5), C_ij = (P_i/P_j) q_i.k_j over ancestors-or-self (Eq. 4) and
+ * (I+G)^{-1} = sum_{m=0..d} (-G)^m, d the tree depth (Lemma 3, Eq. 6).  After
+ * acceptance, the accepted path a is committed as S_new = P_a S_pre +
+ * (D_a K_a)^T U_a (Eq. 10).  Equations are numbered as in the paper; the
+ * LaTeX of Eqs. 1-12 survives in the xllm-io paper review of the same work.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains them after returning.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and runs asynchronously.  Buffers must stay alive until it completes.
+ *  - Host-detectable argument errors return a bole_status synchronously and
+ *    enqueue nothing.  A failed launch returns BOLE_E_HIP.
+ *  - Data-dependent problems found on the device OR bits into *err (a device
+ *    uint32; may be NULL to ignore them).  Outputs of an affected tree or state
+ *    head are then unspecified, but no kernel writes outside that tree's rows,
+ *    that head's G/C tile or that request's state slot.
+ *  - Trees: a flat ragged forest.  Tree b owns global node rows
+ *    [tree_off[b], tree_off[b+1]); tree sizes are 1..64.  parent[] holds the
+ *    LOCAL index of each node's parent inside its tree, -1 for a root.  Any
+ *    acyclic labelling is accepted (parents need not precede children).
+ *  - Token operands are token-major: q, k [N, H, d_k]; v, O, U [N, H, d_v];
+ *    per-node gates [N, H].  Committed states use the serving slot layout
+ *    [slot, H, d_v, d_k] (arXiv page, state-lifecycle paragraph), float32.
+ *  - d_k and d_v are multiples of 16 in [16, 256].
+ *  - Stateless and reentrant: no global state; calls on different streams may
+ *    overlap as long as they do not write the same buffers.
+ */
+#ifndef BOLE_H
+#define BOLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BOLE_API __attribute__((visibility("default")))
+
+/* element type of q/k/v (and of O); gates, states, G/C and U are float32 */
+typedef enum { BOLE_F32 = 0, BOLE_BF16 = 1 } bole_dtype;
+
+typedef enum {
+  BOLE_OK = 0,
+  BOLE_E_NULL = 1,        /* a required pointer is NULL */
+  BOLE_E_SHAPE = 2,       /* a size is out of range */
+  BOLE_E_DTYPE = 3,       /* unknown bole_dtype */
+  BOLE_E_UNSUPPORTED = 4, /* d_k / d_v not a multiple of 16 in [16, 256] */
+  BOLE_E_HIP = 5          /* a HIP launch failed */
+} bole_status;
+
+/* device error bits OR-ed into *err */
+#define BOLE_ERR_BAD_PARENT 1u /* parent out of [-1, T_b) or a node its own parent */
+#define BOLE_ERR_CYCLE 2u      /* parent links contain a cycle */
+#define BOLE_ERR_TREE_SIZE 4u  /* tree_off range empty, larger than 64 or outside [0, N) */
+#define BOLE_ERR_BAD_ACCEPT 8u /* accepted node outside [-1, T_b) */
+#define BOLE_ERR_BAD_SLOT 16u  /* state slot outside [0, n_slots) */
+
+#define BOLE_MAX_TREE 64
+
+/*
+ * bole_tree_prep - round-level topology step plus log-space gate products
+ * (arXiv page: "one round-level topology step followed by three per-layer GPU
+ * stages"; review section 三, fused pipeline, stage (1) gate preparation).
+ *
+ *  in   parent[N]           local parent index per node (-1 = root)
+ *  in   tree_off[B+1]       tree row ranges
+ *  in   log_gamma[L,N,H]    g = log(gamma) per layer/node/head, or NULL
+ *  out  depth[N]            edges to the root (root = 0)
+ *  out  anc[N]              ancestor-or-self bit set, bit j = local node j
+ *  out  order[N]            per tree, local node ids sorted by (depth, id);
+ *                           order[tree_off[b] + p] is the p-th node of tree b
+ *  out  tree_depth[B]       max depth d_b of tree b (Lemma 3's d); -1 marks a
+ *                           tree that failed validation (consumers skip it)
+ *  out  logP[L,N,H]         log P_i = sum of g along the root-to-i path, i
+ *                           included, summed in float32 root first from +0.0f
+ *                           (one rounding per add, no fused ops); NULL iff
+ *                           log_gamma is NULL
+ *  out  err                 BAD_PARENT, CYCLE, TREE_SIZE
+ * Results are bit-exact (integers and the float32 sums alike).
+ */
+BOLE_API int bole_tree_prep(const int32_t* parent, const int32_t* tree_off, int32_t B, int32_t N,
+                   const float* log_gamma, int32_t L, int32_t H, int32_t* depth, uint64_t* anc,
+                   int32_t* order, int32_t* tree_depth, float* logP, uint32_t* err,
+                   void* stream);
+
+/* Bytes of the G plus C workspace for B trees and H heads: 2*B*H*64*64*4. */
+BOLE_API size_t bole_gc_workspace_bytes(int32_t B, int32_t H);
+
+/*
+ * bole_factor_gc - the G/C factor producer, one per (tree, head) (review
+ * section 三, stage (2); Eq. 4 and Eq. 5 of the paper).
+ *
+ *  in   q, k [N,H,d_k]      dtype elements
+ *  in   logP[N,H], beta[N,H] float32 (this layer)
+ *  in   anc[N], tree_off[B+1] from bole_tree_prep
+ *  out  G, C [B,H,64,64]    float32, local node indices:
+ *         G[b,h,i,j] = beta_i exp(logP_i - logP_j) k_i.k_j  for j a strict ancestor of i
+ *         C[b,h,i,j] = exp(logP_i - logP_j) q_i.k_j         for j an ancestor of i or i
+ *       every other entry (including rows/cols >= T_b) is exactly 0.
+ *       Dot products run on bf16 MFMA with float32 accumulation (float32
+ *       operands are split into bf16 hi+lo parts).
+ *  out  err                 TREE_SIZE
+ * G and C are per-layer scratch; they can be reused across layers and rounds.
+ */
+BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const float* logP,
+                   const float* beta, const uint64_t* anc, const int32_t* tree_off, int32_t B,
+                   int32_t N, int32_t H, int32_t d_k, float* G, float* C, uint32_t* err,
+                   void* stream);
+
+/*
+ * bole_verify - value-tiled solve and readout (arXiv page section IV-B; review
+ * Eqs. 7 and 8), one layer.
+ *
+ * For each (tree b, head h, value tile r) it forms
+ *     B0 = D_P Q S_pre^(r),  R = D_beta (V^(r) - D_P K S_pre^(r)),
+ * propagates U = sum_{m=0..d_b} (-G)^m R with the d_b-step finite Neumann
+ * recursion Z <- -G Z, U += Z (on chip), and reads out O^(r) = B0 + C U.
+ *
+ *  in   q, k [N,H,d_k], v [N,H,d_v]   dtype
+ *  in   logP[N,H], beta[N,H]          float32
+ *  in   state_pool[n_slots,H,d_v,d_k] float32, read only (S_pre is immutable)
+ *  in   slot[B]                       state slot of each request
+ *  in   G, C [B,H,64,64]              from bole_factor_gc (this layer)
+ *  in   anc[N], depth[N], tree_off[B+1], tree_depth[B] from bole_tree_prep
+ *  out  O [N,H,d_v]                   dtype
+ *  out  U [N,H,d_v]                   float32, the compact per-node update u_i
+ *  out  err                           TREE_SIZE, BAD_SLOT
+ * O and U must not alias any input.
+ */
+BOLE_API int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
+                const float* beta, const float* state_pool, int32_t n_slots, const int32_t* slot,
+                const float* G, const float* C, const uint64_t* anc, const int32_t* depth,
+                const int32_t* tree_off, const int32_t* tree_depth, int32_t B, int32_t N,
+                int32_t H, int32_t d_k, int32_t d_v, void* O, float* U, uint32_t* err,
+                void* stream);
+
+/*
+ * bole_commit_path - accepted-path state reconstruction for L layers in one
+ * launch, in place (paper Eq. 10; review: unified cross-layer state commit).
+ *
+ * For each layer l, request b and head h, with a = accept[b] and the path
+ * A(a)+{a}:
+ *     S[v][c] <- exp(logP_a) S[v][c] + sum_j exp(logP_a - logP_j) U_j[v] k_j[c]
+ * The path outer products run on bf16 MFMA with float32 accumulation
+ * (float32 operands split into bf16 hi+lo parts).  accept[b] == -1 leaves the
+ * slot bit-unchanged.
+ *
+ *  in/out state_pool + l*state_layer_stride : [n_slots,H,d_v,d_k] float32
+ *  in     k + l*k_layer_stride              : [N,H,d_k] dtype
+ *  in     U + l*u_layer_stride              : [N,H,d_v] float32
+ *  in     logP + l*logp_layer_stride        : [N,H] float32
+ *  in     slot[B], anc[N], tree_off[B+1], accept[B] (local node or -1)
+ *  out    err                               TREE_SIZE, BAD_ACCEPT, BAD_SLOT
+ * Strides are in elements.  Must not run concurrently with a verify that reads
+ * the same slots (order them on one stream).  Two requests must not share a
+ * slot.
+ */
+BOLE_API int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,
+                     const int32_t* slot, int32_t dtype, const void* k, int64_t k_layer_stride,
+                     const float* U, int64_t u_layer_stride, const float* logP,
+                     int64_t logp_layer_stride, const uint64_t* anc, const int32_t* tree_off,
+                     const int32_t* accept, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                     int32_t d_v, uint32_t* err, void* stream);
+
+/* Static description of a bole_status code. */
+BOLE_API const char* bole_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BOLE_H */

@@ -1,0 +1,19 @@
+"""Closed-form tree verification for Gated DeltaNet layers on AMD MI355X (gfx950).
+
+The compute path is libbole.so (hand-written HIP kernels behind the C ABI in
+include/bole.h); this package is its thin Python binding plus device-buffer
+plumbing.  Importing it does not load the library; the first call does, and
+fails loudly if the library has not been built.
+"""
+
+from .bole import (  # noqa: F401
+    BOLE_BF16, BOLE_F32, ERR_BAD_ACCEPT, ERR_BAD_PARENT, ERR_BAD_SLOT, ERR_CYCLE,
+    ERR_TREE_SIZE, MAX_TREE, BoleError, bole_commit_path, bole_factor_gc,
+    bole_gc_workspace_bytes, bole_status_string, bole_tree_prep, bole_verify, lib,
+)
+from .runner import Topology, TreeRound  # noqa: F401
+
+__all__ = [
+    "bole_tree_prep", "bole_factor_gc", "bole_verify", "bole_commit_path",
+    "bole_gc_workspace_bytes", "bole_status_string", "BoleError", "TreeRound", "Topology", "lib",
+]

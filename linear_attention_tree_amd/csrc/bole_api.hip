@@ -1,0 +1,122 @@
+// C ABI of libbole: host-side argument validation, then one or two kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// global state.
+#include <hip/hip_runtime.h>
+
+#include "bole.h"
+
+extern "C" {
+int bole_tree_prep_launch(const int32_t*, const int32_t*, int32_t, int32_t, const float*,
+                          int32_t, int32_t, int32_t*, uint64_t*, int32_t*, int32_t*, float*,
+                          uint32_t*, hipStream_t);
+int bole_factor_gc_launch(int32_t, const void*, const void*, const float*, const float*,
+                          const uint64_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
+                          float*, float*, uint32_t*, hipStream_t);
+int bole_verify_launch(int32_t, const void*, const void*, const void*, const float*,
+                       const float*, const float*, int32_t, const int32_t*, const float*,
+                       const float*, const uint64_t*, const int32_t*, const int32_t*,
+                       const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                       float*, uint32_t*, hipStream_t);
+int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
+                       int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
+                       const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
+                       int32_t, uint32_t*, hipStream_t);
+}
+
+namespace {
+
+constexpr int32_t kMaxGrid = 1 << 30;
+
+bool head_dim_ok(int32_t d) { return d >= 16 && d <= 256 && d % 16 == 0; }
+
+bool dtype_ok(int32_t dt) { return dt == BOLE_F32 || dt == BOLE_BF16; }
+
+// B * H * tiles must fit a 1-D grid
+bool grid_ok(int64_t B, int64_t H, int64_t tiles) { return B * H * tiles < kMaxGrid; }
+
+}  // namespace
+
+extern "C" {
+
+int bole_tree_prep(const int32_t* parent, const int32_t* tree_off, int32_t B, int32_t N,
+                   const float* log_gamma, int32_t L, int32_t H, int32_t* depth, uint64_t* anc,
+                   int32_t* order, int32_t* tree_depth, float* logP, uint32_t* err,
+                   void* stream) {
+  if (!parent || !tree_off || !depth || !anc || !order || !tree_depth) return BOLE_E_NULL;
+  if (B < 1 || N < 1 || B > (1 << 24)) return BOLE_E_SHAPE;
+  if (log_gamma) {
+    if (!logP) return BOLE_E_NULL;
+    if (L < 1 || H < 1 || (int64_t)L * H > (1 << 24)) return BOLE_E_SHAPE;
+  }
+  return bole_tree_prep_launch(parent, tree_off, B, N, log_gamma, L, H, depth, anc, order,
+                               tree_depth, log_gamma ? logP : nullptr, err,
+                               (hipStream_t)stream);
+}
+
+size_t bole_gc_workspace_bytes(int32_t B, int32_t H) {
+  if (B < 1 || H < 1) return 0;
+  return (size_t)2 * B * H * BOLE_MAX_TREE * BOLE_MAX_TREE * sizeof(float);
+}
+
+int bole_factor_gc(int32_t dtype, const void* q, const void* k, const float* logP,
+                   const float* beta, const uint64_t* anc, const int32_t* tree_off, int32_t B,
+                   int32_t N, int32_t H, int32_t d_k, float* G, float* C, uint32_t* err,
+                   void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !logP || !beta || !anc || !tree_off || !G || !C) return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || !grid_ok(B, H, 1)) return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k)) return BOLE_E_UNSUPPORTED;
+  return bole_factor_gc_launch(dtype, q, k, logP, beta, anc, tree_off, B, N, H, d_k, G, C, err,
+                               (hipStream_t)stream);
+}
+
+int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
+                const float* beta, const float* state_pool, int32_t n_slots, const int32_t* slot,
+                const float* G, const float* C, const uint64_t* anc, const int32_t* depth,
+                const int32_t* tree_off, const int32_t* tree_depth, int32_t B, int32_t N,
+                int32_t H, int32_t d_k, int32_t d_v, void* O, float* U, uint32_t* err,
+                void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !G || !C || !anc || !depth ||
+      !tree_off || !tree_depth || !O || !U)
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 4)) return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return BOLE_E_UNSUPPORTED;
+  return bole_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, anc,
+                            depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U, err,
+                            (hipStream_t)stream);
+}
+
+int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,
+                     const int32_t* slot, int32_t dtype, const void* k, int64_t k_layer_stride,
+                     const float* U, int64_t u_layer_stride, const float* logP,
+                     int64_t logp_layer_stride, const uint64_t* anc, const int32_t* tree_off,
+                     const int32_t* accept, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                     int32_t d_v, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!state_pool || !slot || !k || !U || !logP || !anc || !tree_off || !accept)
+    return BOLE_E_NULL;
+  if (L < 1 || L > 65535 || B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 1))
+    return BOLE_E_SHAPE;
+  if (state_layer_stride < 0 || k_layer_stride < 0 || u_layer_stride < 0 ||
+      logp_layer_stride < 0)
+    return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return BOLE_E_UNSUPPORTED;
+  return bole_commit_launch(L, state_pool, state_layer_stride, n_slots, slot, dtype, k,
+                            k_layer_stride, U, u_layer_stride, logP, logp_layer_stride, anc,
+                            tree_off, accept, B, N, H, d_k, d_v, err, (hipStream_t)stream);
+}
+
+const char* bole_status_string(int code) {
+  switch (code) {
+    case BOLE_OK: return "ok";
+    case BOLE_E_NULL: return "a required pointer is NULL";
+    case BOLE_E_SHAPE: return "a size argument is out of range";
+    case BOLE_E_DTYPE: return "unknown element type";
+    case BOLE_E_UNSUPPORTED: return "head dimension must be a multiple of 16 in [16, 256]";
+    case BOLE_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels of libbole.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bole.h"
+
+namespace bole {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMaxTree = BOLE_MAX_TREE;  // one wave64 lane / one mask bit per node
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// MFMA: v_mfma_f32_16x16x32_bf16 (CDNA4).  Lane layout, lane l in [0, 64):
+//   A (16 x 32, row-major M x K): lane holds A[l % 16][8*(l/16) .. 8*(l/16)+7]
+//   B (32 x 16, K x N):           lane holds B[8*(l/16) .. +7][l % 16]
+//   D (16 x 16):                  lane holds D[4*(l/16) + r][l % 16], r = 0..3
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+  return z;
+}
+
+// Round-to-nearest-even split of 8 floats into bf16 hi + lo parts, x ~= hi + lo
+// (relative residual below 2^-16).
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - (float)h);
+  }
+}
+
+__device__ __forceinline__ void load_f32x8(const float* __restrict__ p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* __restrict__ p) {
+  const u16x8 u = *reinterpret_cast<const u16x8*>(p);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Make a value provably wave-uniform for the compiler (scalar registers).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// Workgroup-id remap so that consecutive logical ids land on the same XCD.
+// MI355X dispatches workgroup w to XCD (w mod 8); this returns the logical id
+// whose XCD-local rank is w / 8, with XCD x owning a contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  constexpr int kXcd = 8;
+  const int x = w % kXcd, k = w / kXcd;
+  const int q = total / kXcd, rem = total % kXcd;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
+}  // namespace bole

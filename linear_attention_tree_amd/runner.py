@@ -1,0 +1,91 @@
+"""Device-buffer plumbing around the four calls of libbole.
+
+``TreeRound`` owns the per-round topology buffers of one packed forest and the
+per-layer G/C workspace, allocates outputs with PyTorch and issues the calls in
+stream order.  It performs no arithmetic of its own.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import bole
+
+
+@dataclass
+class Topology:
+    parent: torch.Tensor      # [N] int32
+    tree_off: torch.Tensor    # [B+1] int32
+    depth: torch.Tensor       # [N] int32
+    anc: torch.Tensor         # [N] int64 (uint64 bits)
+    order: torch.Tensor       # [N] int32
+    tree_depth: torch.Tensor  # [B] int32
+
+    @property
+    def B(self) -> int:
+        return self.tree_off.shape[0] - 1
+
+    @property
+    def N(self) -> int:
+        return self.parent.shape[0]
+
+
+class TreeRound:
+    """One verification round over a packed forest on one device."""
+
+    def __init__(self, parent, tree_off, H: int, device="cuda", err: Optional[torch.Tensor] = None):
+        dev = torch.device(device)
+        parent = torch.as_tensor(parent, dtype=torch.int32).to(dev)
+        tree_off = torch.as_tensor(tree_off, dtype=torch.int32).to(dev)
+        N, B = parent.shape[0], tree_off.shape[0] - 1
+        self.H = H
+        self.device = dev
+        self.topo = Topology(parent=parent, tree_off=tree_off,
+                             depth=torch.empty(N, dtype=torch.int32, device=dev),
+                             anc=torch.empty(N, dtype=torch.int64, device=dev),
+                             order=torch.empty(N, dtype=torch.int32, device=dev),
+                             tree_depth=torch.empty(B, dtype=torch.int32, device=dev))
+        self.err = err if err is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        self.G = torch.empty(B, H, bole.MAX_TREE, bole.MAX_TREE, dtype=torch.float32, device=dev)
+        self.C = torch.empty_like(self.G)
+
+    def prep(self, log_gamma: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+        """Topology plus logP for all layers of log_gamma [L, N, H]; returns logP."""
+        t = self.topo
+        logP = None if log_gamma is None else torch.empty_like(log_gamma)
+        bole.bole_tree_prep(t.parent, t.tree_off, log_gamma, t.depth, t.anc, t.order,
+                            t.tree_depth, logP, self.err, stream)
+        return logP
+
+    def factor(self, q, k, logP, beta, stream=None):
+        t = self.topo
+        bole.bole_factor_gc(q, k, logP, beta, t.anc, t.tree_off, self.G, self.C, self.err, stream)
+
+    def verify(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None):
+        t = self.topo
+        N, H, _ = q.shape
+        d_v = v.shape[2]
+        if O is None:
+            O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
+        if U is None:
+            U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
+        bole.bole_verify(q, k, v, logP, beta, state_pool, slot, self.G, self.C, t.anc, t.depth,
+                         t.tree_off, t.tree_depth, O, U, self.err, stream)
+        return O, U
+
+    def layer(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None):
+        """Factor producer then value-tiled verify for one layer."""
+        self.factor(q, k, logP, beta, stream)
+        return self.verify(q, k, v, logP, beta, state_pool, slot, O, U, stream)
+
+    def commit(self, state_pool, slot, k, U, logP, accept, stream=None):
+        t = self.topo
+        accept = torch.as_tensor(accept, dtype=torch.int32).to(self.device)
+        bole.bole_commit_path(state_pool, slot, k, U, logP, t.anc, t.tree_off, accept,
+                              self.err, stream)
+
+    def error_bits(self) -> int:
+        return int(self.err.item()) & 0xFFFFFFFF

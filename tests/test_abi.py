@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+Every entry point validates its arguments before touching the HIP runtime, so
+these calls return synchronously with a status code.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_tree_amd as lat
+from linear_attention_tree_amd import bole
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bole.h")
+
+E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED = 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"BOLE_API\s+[\w\s\*]+?\b(bole_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bole.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
+                          "bole_verify", "bole_commit_path", "bole_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+        assert hasattr(lat, n), n   # same names in the Python binding
+
+
+def test_internal_launchers_are_hidden(L):
+    for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch"):
+        with pytest.raises(AttributeError):
+            getattr(L, n)
+
+
+def test_status_strings_and_workspace(L):
+    assert lat.bole_status_string(0) == "ok"
+    assert "NULL" in lat.bole_status_string(1)
+    assert lat.bole_status_string(77) == "unknown status"
+    assert lat.bole_gc_workspace_bytes(16, 32) == 2 * 16 * 32 * 64 * 64 * 4
+    assert lat.bole_gc_workspace_bytes(0, 32) == 0
+
+
+def test_tree_prep_argument_errors(L):
+    f = L.bole_tree_prep
+    assert f(None, FAKE, 1, 1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None, None) == E_NULL
+    assert f(FAKE, FAKE, 0, 1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None, None) == E_SHAPE
+    assert f(FAKE, FAKE, 1, 0, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None, None) == E_SHAPE
+    # gates without a logP output
+    assert f(FAKE, FAKE, 1, 1, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, None, None, None) == E_NULL
+    assert f(FAKE, FAKE, 1, 1, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == E_SHAPE
+
+
+def test_factor_gc_argument_errors(L):
+    f = L.bole_factor_gc
+    args = [FAKE] * 6
+    assert f(7, *args, 1, 1, 1, 128, FAKE, FAKE, None, None) == E_DTYPE
+    assert f(1, None, *args[1:], 1, 1, 1, 128, FAKE, FAKE, None, None) == E_NULL
+    assert f(1, *args, 1, 1, 0, 128, FAKE, FAKE, None, None) == E_SHAPE
+    for dk in (0, 8, 24, 272):
+        assert f(1, *args, 1, 1, 1, dk, FAKE, FAKE, None, None) == E_UNSUPPORTED
+
+
+def _verify(L, dtype=1, B=1, N=1, H=1, dk=128, dv=128, n_slots=1, O=FAKE):
+    p = [FAKE] * 6
+    return L.bole_verify(dtype, *p, n_slots, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         B, N, H, dk, dv, O, FAKE, None, None)
+
+
+def test_verify_argument_errors(L):
+    assert _verify(L, dtype=2) == E_DTYPE
+    assert _verify(L, O=None) == E_NULL
+    assert _verify(L, B=0) == E_SHAPE
+    assert _verify(L, n_slots=0) == E_SHAPE
+    assert _verify(L, dv=100) == E_UNSUPPORTED
+    assert _verify(L, dk=512) == E_UNSUPPORTED
+
+
+def test_commit_argument_errors(L):
+    f = L.bole_commit_path
+
+    def call(Lyr=1, dtype=1, stride=0, B=1, dk=128, acc=FAKE):
+        return f(Lyr, FAKE, stride, 1, FAKE, dtype, FAKE, 0, FAKE, 0, FAKE, 0, FAKE, FAKE, acc,
+                 B, 1, 1, dk, 128, None, None)
+
+    assert call(dtype=5) == E_DTYPE
+    assert call(acc=None) == E_NULL
+    assert call(Lyr=0) == E_SHAPE
+    assert call(stride=-1) == E_SHAPE
+    assert call(B=0) == E_SHAPE
+    assert call(dk=20) == E_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        lat.bole_tree_prep(t, t, None, t, t.long(), t, t, None)

@@ -12,18 +12,19 @@ recursive trees with a depth cap, which stand in for the drafter-built proposal
 trees of the paper's evaluation (no drafter or dataset is used).
 
 Value distributions (per node and head):
-  q, k ~ N(0, 1), then L2-normalised over the key dimension (in float64),
+  q, k ~ N(0, 1), then L2-normalised over the key dimension,
   v ~ N(0, 1),
   g = log(gamma) = -softplus(x) with x ~ N(mu_x, 1)  (mu_x = 0, or -3 for the
       deep-chain stress setting so that gamma sits near 1),
   beta = sigmoid(N(0, 1)).
-All values are generated in float64, then rounded to float32 (round to nearest
-even) and, for bf16 workloads, q/k/v further to bfloat16 (round to nearest even).
+q, k, v are drawn and normalised in float32; gates are computed in float64 and
+rounded to float32.  For bf16 workloads q/k/v are then rounded to bfloat16
+(round to nearest even).  Both sides receive exactly these stored values.
 """
 
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -89,24 +90,38 @@ def _rng(seed: int, cfg: Config, stream: int, *more: int) -> np.random.Generator
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest even); returns the uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite value in workload")
+    u = x.view(np.uint32)
+    # finite inputs cannot carry past bit 31
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def round_storage(x: np.ndarray, dtype: str):
-    """float64 -> (storage array, float64 view of exactly the stored values)."""
-    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float -> storage array (float32, or uint16 bfloat16 bit patterns)."""
+    x32 = np.asarray(x).astype(np.float32, copy=False)
     if dtype == "f32":
-        return x32, x32.astype(np.float64)
+        return np.ascontiguousarray(x32)
     if dtype == "bf16":
-        bits = f32_to_bf16_bits(x32)
-        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+        return f32_to_bf16_bits(x32)
     raise ValueError(dtype)
+
+
+def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array -> float64 copy of exactly the stored values."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(stored).astype(np.float64)
+    return np.asarray(stored, dtype=np.float64)
+
+
+def round_storage(x: np.ndarray, dtype: str):
+    """float -> (storage array, float64 view of exactly the stored values)."""
+    st = to_storage(x, dtype)
+    return st, widen(st, dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -172,8 +187,9 @@ def make_forest(cfg: Config, seed: int = 0) -> Forest:
 # per-layer token operands
 
 def _unit_rows(rng, n, d):
-    x = rng.standard_normal((n, d))
-    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+    x = rng.standard_normal((n, d), dtype=np.float32)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return x
 
 
 def _gates(rng, shape, mu):
@@ -191,10 +207,19 @@ class LayerInputs:
     v: np.ndarray
     g: np.ndarray           # [N, H] float32, log of the decay gate
     beta: np.ndarray        # [N, H] float32
-    q64: np.ndarray         # float64 copies of exactly the stored values
-    k64: np.ndarray
-    v64: np.ndarray
     dtype: str
+
+    @property
+    def q64(self):          # float64 copies of exactly the stored values
+        return widen(self.q, self.dtype)
+
+    @property
+    def k64(self):
+        return widen(self.k, self.dtype)
+
+    @property
+    def v64(self):
+        return widen(self.v, self.dtype)
 
     @property
     def g64(self):
@@ -210,14 +235,11 @@ def make_layer(cfg: Config, N: int, layer: int = 0, seed: int = 0) -> LayerInput
     H = cfg.H
     q = _unit_rows(rng, N * H, cfg.d_k).reshape(N, H, cfg.d_k)
     k = _unit_rows(rng, N * H, cfg.d_k).reshape(N, H, cfg.d_k)
-    v = rng.standard_normal((N, H, cfg.d_v))
+    v = rng.standard_normal((N, H, cfg.d_v), dtype=np.float32)
     g, beta = _gates(rng, (N, H), cfg.gate_mu)
-    qs, q64 = round_storage(q, cfg.dtype)
-    ks, k64 = round_storage(k, cfg.dtype)
-    vs, v64 = round_storage(v, cfg.dtype)
-    return LayerInputs(q=qs, k=ks, v=vs, g=g.astype(np.float32),
-                       beta=beta.astype(np.float32), q64=q64, k64=k64, v64=v64,
-                       dtype=cfg.dtype)
+    return LayerInputs(q=to_storage(q, cfg.dtype), k=to_storage(k, cfg.dtype),
+                       v=to_storage(v, cfg.dtype), g=g.astype(np.float32),
+                       beta=beta.astype(np.float32), dtype=cfg.dtype)
 
 
 @dataclass
@@ -238,7 +260,7 @@ def make_prefix(cfg: Config, layer: int, b: int, h: int, seed: int = 0) -> Prefi
     P = cfg.prefix
     q = _unit_rows(rng, P, cfg.d_k)
     k = _unit_rows(rng, P, cfg.d_k)
-    v = rng.standard_normal((P, cfg.d_v))
+    v = rng.standard_normal((P, cfg.d_v), dtype=np.float32)
     g, beta = _gates(rng, (P,), cfg.gate_mu)
     return PrefixTokens(q64=round_storage(q, cfg.dtype)[1], k64=round_storage(k, cfg.dtype)[1],
                         v64=round_storage(v, cfg.dtype)[1],
@@ -259,3 +281,27 @@ def forest_from_trees(trees: List[np.ndarray], accept: Optional[List[int]] = Non
     off[1:] = np.cumsum([len(t) for t in trees])
     acc = np.array(accept if accept is not None else [len(t) - 1 for t in trees], dtype=np.int32)
     return Forest(parent=np.concatenate(trees).astype(np.int32), tree_off=off, accept=acc)
+
+
+@dataclass
+class PrefixBulk:
+    """Committed-prefix tokens of all B x H state heads of one layer, [P, B, H, d]
+    (storage arrays as for LayerInputs).  Drawn from one stream per layer; the
+    per-head generator ``make_prefix`` serves the oracle-checked tests."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray       # [P, B, H] float32
+    beta: np.ndarray    # [P, B, H] float32
+
+
+def make_prefix_bulk(cfg: Config, B: int, layer: int = 0, seed: int = 0) -> PrefixBulk:
+    rng = _rng(seed, cfg, STREAM_PREFIX, layer, 1 << 20)
+    P, H = cfg.prefix, cfg.H
+    q = _unit_rows(rng, P * B * H, cfg.d_k).reshape(P, B, H, cfg.d_k)
+    k = _unit_rows(rng, P * B * H, cfg.d_k).reshape(P, B, H, cfg.d_k)
+    v = rng.standard_normal((P, B, H, cfg.d_v), dtype=np.float32)
+    g, beta = _gates(rng, (P, B, H), cfg.gate_mu)
+    return PrefixBulk(q=to_storage(q, cfg.dtype), k=to_storage(k, cfg.dtype),
+                      v=to_storage(v, cfg.dtype), g=g.astype(np.float32),
+                      beta=beta.astype(np.float32))
