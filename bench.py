@@ -114,26 +114,68 @@ class InputSet:
         self.U = torch.empty(N, H, cfg.d_v, dtype=torch.float32, device=dev)
 
 
-def run_step(s, bole, events=None):
-    """prep -> factor -> verify -> commit on the current stream."""
+def launch(s, bole, which):
     t = s.rnd.topo
-    if events:
-        events[0].record()
-    bole.bole_tree_prep(t.parent, t.tree_off, s.g, t.depth, t.anc, t.order, t.tree_depth,
-                        s.logP, s.rnd.err)
-    if events:
-        events[1].record()
     lp = s.logP[0]
-    bole.bole_factor_gc(s.q, s.k, lp, s.beta, t.anc, t.tree_off, s.rnd.G, s.rnd.C, s.rnd.err)
-    if events:
-        events[2].record()
-    bole.bole_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C, t.anc, t.depth,
-                     t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
-    if events:
-        events[3].record()
-    bole.bole_commit_path(s.pool, s.slot, s.k, s.U, lp, t.anc, t.tree_off, s.accept, s.rnd.err)
-    if events:
-        events[4].record()
+    if which == "tree_prep":
+        bole.bole_tree_prep(t.parent, t.tree_off, s.g, t.depth, t.anc, t.order, t.tree_depth,
+                            s.logP, s.rnd.err)
+    elif which == "factor_gc":
+        bole.bole_factor_gc(s.q, s.k, lp, s.beta, t.anc, t.order, t.tree_off, s.rnd.G, s.rnd.C,
+                            s.rnd.err)
+    elif which == "verify":
+        bole.bole_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C, t.order,
+                         t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
+    elif which == "factor_verify":
+        bole.bole_factor_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, t.anc, t.order,
+                                t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
+    elif which == "commit":
+        bole.bole_commit_path(s.pool, s.slot, s.k, s.U, lp, t.anc, t.tree_off, s.accept,
+                              s.rnd.err)
+    else:
+        raise ValueError(which)
+
+
+STEPS = {
+    # G/C produced and consumed in one launch (the default)
+    "fused": ("tree_prep", "factor_verify", "commit"),
+    # the four-call path: G/C written by the producer, read back by verify
+    "split": ("tree_prep", "factor_gc", "verify", "commit"),
+}
+
+
+def run_step(s, bole, path="fused"):
+    """One pass of the whole path on the current stream."""
+    for which in STEPS[path]:
+        launch(s, bole, which)
+
+
+def time_steps(sets, bole, path, K, torch):
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        run_step(sets[i % len(sets)], bole, path)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / K
+
+
+def time_kernel(sets, bole, which, reps, torch):
+    """Average duration of one launch of `which`, back to back over the rotated
+    input sets, bracketed by events on the launching (current) stream."""
+    for i in range(len(sets)):
+        launch(sets[i], bole, which)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        launch(sets[i % len(sets)], bole, which)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline(cfg, seed, budget_s=12.0):
@@ -169,6 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="target", choices=sorted(W.CONFIGS))
     ap.add_argument("--sets", type=int, default=4, help="rotated independent input sets")
+    ap.add_argument("--path", default="fused", choices=sorted(STEPS),
+                    help="fused: prep + factor_verify + commit; split: the four calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -188,30 +232,27 @@ def main():
     e = 2 if cfg.dtype == "bf16" else 4
 
     for i in range(args.warmup):
-        run_step(sets[i % len(sets)], bole)
+        run_step(sets[i % len(sets)], bole, args.path)
+        run_step(sets[i % len(sets)], bole, "split")
     torch.cuda.synchronize()
     for s in sets:
         assert s.rnd.error_bits() == 0, "device error bits set"
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(K):
-        run_step(sets[i % len(sets)], bole, ev[i])
-    t_stop.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    ms_step = total_ms / K
-    per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
-    avg = per.mean(axis=0)          # prep, factor, verify, commit (ms)
+    ms_step = time_steps(sets, bole, args.path, K, torch)
+    other = "split" if args.path == "fused" else "fused"
+    ms_other = time_steps(sets, bole, other, max(K // 2, 10), torch)
+    # per-kernel averages: each kernel alone, back to back (same inputs, same stream)
+    kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "commit")
+    avg = {which: time_kernel(sets, bole, which, max(K, 20), torch) for which in kernels}
+    for s_ in sets:
+        assert s_.rnd.error_bits() == 0, "device error bits set"
+    dominant = "factor_verify" if args.path == "fused" else "verify"
 
     nodes = sum(s.forest.N for s in sets) / len(sets)
     value = nodes * cfg.H / (ms_step * 1e-3)
     vbytes = np.mean([verify_algorithmic_bytes(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
-    achieved = vbytes / (avg[2] * 1e-3) / 1e9
+    achieved = vbytes / (avg[dominant] * 1e-3) / 1e9
     traffic = traffic_from_profile(kernel_source_hash())
 
     out = {
@@ -230,15 +271,14 @@ def main():
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} trees x T={cfg.T} nodes (random recursive, "
                         f"depth<={cfg.D}), H={cfg.H}, d_k=d_v={cfg.d_k}, {cfg.dtype} q/k/v, "
-                        "f32 gates and state; step = tree_prep + factor_gc + verify + commit",
+                        f"f32 gates and state; step = {' + '.join(STEPS[args.path])}",
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
-            "nodes": nodes, "input_sets": len(sets),
-            "kernel_ms": {"tree_prep": avg[0], "factor_gc": avg[1], "verify": avg[2],
-                          "commit": avg[3]},
-            "layer_ms_factor_plus_verify": avg[1] + avg[2],
+            "nodes": nodes, "input_sets": len(sets), "path": args.path,
+            "ms_per_step_other_path": {other: ms_other},
+            "kernel_ms_back_to_back": avg,
         },
         "roofline": {
-            "kernel": "bole_verify",
+            "kernel": "bole_" + dominant,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,

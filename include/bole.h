@@ -107,20 +107,23 @@ BOLE_API size_t bole_gc_workspace_bytes(int32_t B, int32_t H);
  *
  *  in   q, k [N,H,d_k]      dtype elements
  *  in   logP[N,H], beta[N,H] float32 (this layer)
- *  in   anc[N], tree_off[B+1] from bole_tree_prep
- *  out  G, C [B,H,64,64]    float32, local node indices:
- *         G[b,h,i,j] = beta_i exp(logP_i - logP_j) k_i.k_j  for j a strict ancestor of i
- *         C[b,h,i,j] = exp(logP_i - logP_j) q_i.k_j         for j an ancestor of i or i
- *       every other entry (including rows/cols >= T_b) is exactly 0.
+ *  in   anc[N], order[N], tree_off[B+1] from bole_tree_prep
+ *  out  G, C [B,H,64,64]    float32, indexed by LEVEL-ORDER position: with
+ *       i = order[tree_off[b] + p] and j = order[tree_off[b] + q],
+ *         G[b,h,p,q] = beta_i exp(logP_i - logP_j) k_i.k_j  for j a strict ancestor of i
+ *         C[b,h,p,q] = exp(logP_i - logP_j) q_i.k_j         for j an ancestor of i or i
+ *       every other entry (including rows/cols >= T_b) is exactly 0.  Level
+ *       order puts parents before children, so G is strictly lower triangular
+ *       and C lower triangular (the indexing of the paper's Theorem 1).
  *       Dot products run on bf16 MFMA with float32 accumulation (float32
  *       operands are split into bf16 hi+lo parts).
  *  out  err                 TREE_SIZE
  * G and C are per-layer scratch; they can be reused across layers and rounds.
  */
 BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const float* logP,
-                   const float* beta, const uint64_t* anc, const int32_t* tree_off, int32_t B,
-                   int32_t N, int32_t H, int32_t d_k, float* G, float* C, uint32_t* err,
-                   void* stream);
+                            const float* beta, const uint64_t* anc, const int32_t* order,
+                            const int32_t* tree_off, int32_t B, int32_t N, int32_t H,
+                            int32_t d_k, float* G, float* C, uint32_t* err, void* stream);
 
 /*
  * bole_verify - value-tiled solve and readout (arXiv page section IV-B; review
@@ -130,13 +133,15 @@ BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const f
  *     B0 = D_P Q S_pre^(r),  R = D_beta (V^(r) - D_P K S_pre^(r)),
  * propagates U = sum_{m=0..d_b} (-G)^m R with the d_b-step finite Neumann
  * recursion Z <- -G Z, U += Z (on chip), and reads out O^(r) = B0 + C U.
+ * All products run on bf16 MFMA with float32 accumulation; float32 operands
+ * (states, G, C, Z, U, and float32 q/k) are split into bf16 hi+lo parts.
  *
  *  in   q, k [N,H,d_k], v [N,H,d_v]   dtype
  *  in   logP[N,H], beta[N,H]          float32
  *  in   state_pool[n_slots,H,d_v,d_k] float32, read only (S_pre is immutable)
  *  in   slot[B]                       state slot of each request
  *  in   G, C [B,H,64,64]              from bole_factor_gc (this layer)
- *  in   anc[N], depth[N], tree_off[B+1], tree_depth[B] from bole_tree_prep
+ *  in   order[N], depth[N], tree_off[B+1], tree_depth[B] from bole_tree_prep
  *  out  O [N,H,d_v]                   dtype
  *  out  U [N,H,d_v]                   float32, the compact per-node update u_i
  *  out  err                           TREE_SIZE, BAD_SLOT
@@ -144,10 +149,30 @@ BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const f
  */
 BOLE_API int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
                 const float* beta, const float* state_pool, int32_t n_slots, const int32_t* slot,
-                const float* G, const float* C, const uint64_t* anc, const int32_t* depth,
+                const float* G, const float* C, const int32_t* order, const int32_t* depth,
                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B, int32_t N,
                 int32_t H, int32_t d_k, int32_t d_v, void* O, float* U, uint32_t* err,
                 void* stream);
+
+/*
+ * bole_factor_verify - bole_factor_gc and bole_verify in one launch.  With
+ * d_v <= 128 a head's value columns form one workgroup, so the factors have a
+ * single consumer; here the Gram products and their masked epilogue run inside
+ * the verify workgroup from the Q/K rows it stages anyway, and G/C never touch
+ * memory.  The arithmetic is the same as the two-call path, so O and U are
+ * bit-identical to bole_factor_gc followed by bole_verify.
+ *
+ *  arguments as bole_verify, with anc[N] (from bole_tree_prep) in place of G, C.
+ *  d_k must not exceed 128 for bf16 and 64 for float32 token inputs
+ *  (BOLE_E_UNSUPPORTED otherwise; the two-call path has no such limit).
+ */
+BOLE_API int bole_factor_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                                const float* logP, const float* beta, const float* state_pool,
+                                int32_t n_slots, const int32_t* slot, const uint64_t* anc,
+                                const int32_t* order, const int32_t* depth,
+                                const int32_t* tree_off, const int32_t* tree_depth, int32_t B,
+                                int32_t N, int32_t H, int32_t d_k, int32_t d_v, void* O, float* U,
+                                uint32_t* err, void* stream);
 
 /*
  * bole_commit_path - accepted-path state reconstruction for L layers in one

@@ -11,7 +11,8 @@ Tensor conventions (see bole.h for the full contract):
   err [1] int32 (the device uint32 error word), or None
   q, k [N, H, d_k], v [N, H, d_v] in float32 or bfloat16
   logP, beta [N, H] float32; state_pool [n_slots, H, d_v, d_k] float32
-  G, C [B, H, 64, 64] float32; O [N, H, d_v] like v; U [N, H, d_v] float32
+  G, C [B, H, 64, 64] float32 (level-order positions); O [N, H, d_v] like v;
+  U [N, H, d_v] float32
 """
 
 from __future__ import annotations
@@ -52,10 +53,13 @@ def lib() -> ctypes.CDLL:
         L.bole_gc_workspace_bytes.restype = ctypes.c_size_t
         L.bole_gc_workspace_bytes.argtypes = [i32, i32]
         L.bole_factor_gc.restype = ctypes.c_int
-        L.bole_factor_gc.argtypes = [i32, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, P]
+        L.bole_factor_gc.argtypes = [i32, P, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, P]
         L.bole_verify.restype = ctypes.c_int
         L.bole_verify.argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P, P]
                                   + [i32] * 5 + [P, P, P, P])
+        L.bole_factor_verify.restype = ctypes.c_int
+        L.bole_factor_verify.argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P]
+                                         + [i32] * 5 + [P, P, P, P])
         L.bole_commit_path.restype = ctypes.c_int
         L.bole_commit_path.argtypes = [i32, P, i64, i32, P, i32, P, i64, P, i64, P, i64, P, P,
                                        P, i32, i32, i32, i32, i32, P, P]
@@ -149,7 +153,7 @@ def bole_tree_prep(parent, tree_off, log_gamma, depth, anc, order, tree_depth, l
         _ptr(err), _stream(stream)))
 
 
-def bole_factor_gc(q, k, logP, beta, anc, tree_off, G, C, err=None, stream=None):
+def bole_factor_gc(q, k, logP, beta, anc, order, tree_off, G, C, err=None, stream=None):
     _need(q, "q", (torch.float32, torch.bfloat16), 3)
     _need(k, "k", q.dtype, 3)
     N, H, d_k = q.shape
@@ -161,18 +165,21 @@ def bole_factor_gc(q, k, logP, beta, anc, tree_off, G, C, err=None, stream=None)
         if tuple(t.shape) != (N, H):
             raise ValueError(f"{nm} must be [N, H]")
     _need(anc, "anc", torch.int64, 1)
+    _need(order, "order", torch.int32, 1)
     _need(tree_off, "tree_off", torch.int32, 1)
+    if anc.shape[0] != N or order.shape[0] != N:
+        raise ValueError("anc and order need N entries")
     for t, nm in ((G, "G"), (C, "C")):
         _need(t, nm, torch.float32, 4)
         if tuple(t.shape) != (B, H, MAX_TREE, MAX_TREE):
             raise ValueError(f"{nm} must be [B, H, 64, 64]")
     _need(err, "err", torch.int32, 1, allow_none=True)
     _check("bole_factor_gc", lib().bole_factor_gc(
-        _code(q.dtype), _ptr(q), _ptr(k), _ptr(logP), _ptr(beta), _ptr(anc), _ptr(tree_off),
-        B, N, H, d_k, _ptr(G), _ptr(C), _ptr(err), _stream(stream)))
+        _code(q.dtype), _ptr(q), _ptr(k), _ptr(logP), _ptr(beta), _ptr(anc), _ptr(order),
+        _ptr(tree_off), B, N, H, d_k, _ptr(G), _ptr(C), _ptr(err), _stream(stream)))
 
 
-def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, anc, depth, tree_off, tree_depth,
+def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_off, tree_depth,
                 O, U, err=None, stream=None):
     _need(q, "q", (torch.float32, torch.bfloat16), 3)
     _need(k, "k", q.dtype, 3)
@@ -194,10 +201,12 @@ def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, anc, depth, tree_of
         _need(t, nm, torch.float32, 4)
         if tuple(t.shape) != (B, H, MAX_TREE, MAX_TREE):
             raise ValueError(f"{nm} must be [B, H, 64, 64]")
-    _need(anc, "anc", torch.int64, 1)
+    _need(order, "order", torch.int32, 1)
     _need(depth, "depth", torch.int32, 1)
     _need(tree_off, "tree_off", torch.int32, 1)
     _need(tree_depth, "tree_depth", torch.int32, 1)
+    if order.shape[0] != N or depth.shape[0] != N:
+        raise ValueError("order and depth need N entries")
     _need(O, "O", v.dtype, 3)
     _need(U, "U", torch.float32, 3)
     if tuple(O.shape) != (N, H, d_v) or tuple(U.shape) != (N, H, d_v):
@@ -207,9 +216,48 @@ def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, anc, depth, tree_of
     _need(err, "err", torch.int32, 1, allow_none=True)
     _check("bole_verify", lib().bole_verify(
         _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(logP), _ptr(beta), _ptr(state_pool),
-        state_pool.shape[0], _ptr(slot), _ptr(G), _ptr(C), _ptr(anc), _ptr(depth),
+        state_pool.shape[0], _ptr(slot), _ptr(G), _ptr(C), _ptr(order), _ptr(depth),
         _ptr(tree_off), _ptr(tree_depth), B, N, H, d_k, d_v, _ptr(O), _ptr(U), _ptr(err),
         _stream(stream)))
+
+
+def bole_factor_verify(q, k, v, logP, beta, state_pool, slot, anc, order, depth, tree_off,
+                       tree_depth, O, U, err=None, stream=None):
+    """bole_factor_gc + bole_verify in one launch (G/C stay on chip)."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    B = tree_off.shape[0] - 1
+    if tuple(k.shape) != (N, H, d_k) or tuple(v.shape[:2]) != (N, H):
+        raise ValueError("q, k, v shapes disagree")
+    for t, nm in ((logP, "logP"), (beta, "beta")):
+        _need(t, nm, torch.float32, 2)
+        if tuple(t.shape) != (N, H):
+            raise ValueError(f"{nm} must be [N, H]")
+    _need(state_pool, "state_pool", torch.float32, 4)
+    if tuple(state_pool.shape[1:]) != (H, d_v, d_k):
+        raise ValueError("state_pool must be [n_slots, H, d_v, d_k]")
+    _need(slot, "slot", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 1)
+    _need(order, "order", torch.int32, 1)
+    _need(depth, "depth", torch.int32, 1)
+    _need(tree_off, "tree_off", torch.int32, 1)
+    _need(tree_depth, "tree_depth", torch.int32, 1)
+    if anc.shape[0] != N or order.shape[0] != N or depth.shape[0] != N:
+        raise ValueError("anc, order and depth need N entries")
+    _need(O, "O", v.dtype, 3)
+    _need(U, "U", torch.float32, 3)
+    if tuple(O.shape) != (N, H, d_v) or tuple(U.shape) != (N, H, d_v):
+        raise ValueError("O and U must be [N, H, d_v]")
+    if slot.shape[0] != B or tree_depth.shape[0] != B:
+        raise ValueError("slot and tree_depth need B entries")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_factor_verify", lib().bole_factor_verify(
+        _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(logP), _ptr(beta), _ptr(state_pool),
+        state_pool.shape[0], _ptr(slot), _ptr(anc), _ptr(order), _ptr(depth), _ptr(tree_off),
+        _ptr(tree_depth), B, N, H, d_k, d_v, _ptr(O), _ptr(U), _ptr(err), _stream(stream)))
 
 
 def _layer_view(t, name, inner_ndim):

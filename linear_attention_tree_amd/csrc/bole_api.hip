@@ -10,13 +10,19 @@ int bole_tree_prep_launch(const int32_t*, const int32_t*, int32_t, int32_t, cons
                           int32_t, int32_t, int32_t*, uint64_t*, int32_t*, int32_t*, float*,
                           uint32_t*, hipStream_t);
 int bole_factor_gc_launch(int32_t, const void*, const void*, const float*, const float*,
-                          const uint64_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
-                          float*, float*, uint32_t*, hipStream_t);
+                          const uint64_t*, const int32_t*, const int32_t*, int32_t, int32_t,
+                          int32_t, int32_t, float*, float*, uint32_t*, hipStream_t);
 int bole_verify_launch(int32_t, const void*, const void*, const void*, const float*,
                        const float*, const float*, int32_t, const int32_t*, const float*,
-                       const float*, const uint64_t*, const int32_t*, const int32_t*,
+                       const float*, const int32_t*, const int32_t*, const int32_t*,
                        const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
                        float*, uint32_t*, hipStream_t);
+int bole_factor_verify_max_dk(int32_t);
+int bole_factor_verify_launch(int32_t, const void*, const void*, const void*, const float*,
+                              const float*, const float*, int32_t, const int32_t*,
+                              const uint64_t*, const int32_t*, const int32_t*, const int32_t*,
+                              const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                              float*, uint32_t*, hipStream_t);
 int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
@@ -59,32 +65,50 @@ size_t bole_gc_workspace_bytes(int32_t B, int32_t H) {
 }
 
 int bole_factor_gc(int32_t dtype, const void* q, const void* k, const float* logP,
-                   const float* beta, const uint64_t* anc, const int32_t* tree_off, int32_t B,
-                   int32_t N, int32_t H, int32_t d_k, float* G, float* C, uint32_t* err,
-                   void* stream) {
+                   const float* beta, const uint64_t* anc, const int32_t* order,
+                   const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                   float* G, float* C, uint32_t* err, void* stream) {
   if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
-  if (!q || !k || !logP || !beta || !anc || !tree_off || !G || !C) return BOLE_E_NULL;
+  if (!q || !k || !logP || !beta || !anc || !order || !tree_off || !G || !C) return BOLE_E_NULL;
   if (B < 1 || N < 1 || H < 1 || !grid_ok(B, H, 1)) return BOLE_E_SHAPE;
   if (!head_dim_ok(d_k)) return BOLE_E_UNSUPPORTED;
-  return bole_factor_gc_launch(dtype, q, k, logP, beta, anc, tree_off, B, N, H, d_k, G, C, err,
-                               (hipStream_t)stream);
+  return bole_factor_gc_launch(dtype, q, k, logP, beta, anc, order, tree_off, B, N, H, d_k, G,
+                               C, err, (hipStream_t)stream);
 }
 
 int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
                 const float* beta, const float* state_pool, int32_t n_slots, const int32_t* slot,
-                const float* G, const float* C, const uint64_t* anc, const int32_t* depth,
+                const float* G, const float* C, const int32_t* order, const int32_t* depth,
                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B, int32_t N,
                 int32_t H, int32_t d_k, int32_t d_v, void* O, float* U, uint32_t* err,
                 void* stream) {
   if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
-  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !G || !C || !anc || !depth ||
+  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !G || !C || !order || !depth ||
       !tree_off || !tree_depth || !O || !U)
     return BOLE_E_NULL;
   if (B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 4)) return BOLE_E_SHAPE;
   if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return BOLE_E_UNSUPPORTED;
-  return bole_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, anc,
+  return bole_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, order,
                             depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U, err,
                             (hipStream_t)stream);
+}
+
+int bole_factor_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                       const float* logP, const float* beta, const float* state_pool,
+                       int32_t n_slots, const int32_t* slot, const uint64_t* anc,
+                       const int32_t* order, const int32_t* depth, const int32_t* tree_off,
+                       const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                       int32_t d_v, void* O, float* U, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !anc || !order || !depth ||
+      !tree_off || !tree_depth || !O || !U)
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 4)) return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k > bole_factor_verify_max_dk(dtype))
+    return BOLE_E_UNSUPPORTED;
+  return bole_factor_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, anc,
+                                   order, depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U,
+                                   err, (hipStream_t)stream);
 }
 
 int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,

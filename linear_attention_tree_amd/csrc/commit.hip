@@ -4,49 +4,30 @@
 //   S[v][c] <- P_a S[v][c] + sum_{j in path(a)} (P_a/P_j) U_j[v] k_j[c]
 //
 // One workgroup per (layer, request, head).  The path sum is a
-// [d_v x L_a] x [L_a x d_k] product on bf16 MFMA (K = path position, padded to
-// 32): A = (P_a/P_j) U_j (float32, split hi+lo), B = k_j (bf16 exact; float32
-// keys are split as well).  The P_a S term is applied in float32 in the
-// epilogue, so every slot element is read once and written once.
+// [d_k x L_a] x [L_a x d_v] product on v_mfma_f32_16x16x32_bf16 with the path
+// position as K (chunks of 32): A = k_j (bf16 exact; float32 keys split hi+lo),
+// B = (P_a/P_j) U_j (float32, split hi+lo).  The path rows are staged once in
+// LDS, transposed so every fragment is one 16-byte read.  The accumulator of a
+// 16x16 tile holds four consecutive key columns of one value row, which is one
+// float4 of the slot: each slot element is read once (prefetched before the
+// products) and written once, with the P_a S term applied in float32.
 #include "common.h"
 
 namespace bole {
 
-template <int DT>
-__device__ __forceinline__ void load_key8(const void* k, int64_t row_stride_elems,
-                                          const int* pj, int p0, int La, int64_t base, int c,
-                                          bf16x8& hi, bf16x8& lo) {
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int p = p0 + e;
-    float val = 0.0f;
-    if (p < La) {
-      const int64_t idx = base + (int64_t)pj[p] * row_stride_elems + c;
-      if (DT == BOLE_BF16)
-        val = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(k)[idx]);
-      else
-        val = reinterpret_cast<const float*>(k)[idx];
-    }
-    x[e] = val;
-  }
-  if (DT == BOLE_BF16) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hi[e] = (__bf16)x[e];  // exact: values are bf16
-    lo = zero_bf16x8();
-  } else {
-    split_bf16x8(x, hi, lo);
-  }
-}
+constexpr int kCommitThreads = 256;
+constexpr int kPathChunk = 32;             // path positions per K chunk
+constexpr int kPRow = kPathChunk + 8;      // bf16 per transposed LDS row (16 B pad)
 
 template <int DT>
-__global__ __launch_bounds__(256) void commit_kernel(
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     float* __restrict__ state_pool, int64_t state_layer_stride, int32_t n_slots,
     const int32_t* __restrict__ slot, const void* __restrict__ kmat, int64_t k_layer_stride,
     const float* __restrict__ Umat, int64_t u_layer_stride, const float* __restrict__ logP,
     int64_t logp_layer_stride, const uint64_t* __restrict__ anc,
     const int32_t* __restrict__ tree_off, const int32_t* __restrict__ accept, int32_t B,
     int32_t N, int32_t H, int32_t d_k, int32_t d_v, uint32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int pj[kMaxTree];
   __shared__ float wj[kMaxTree];
 
@@ -54,9 +35,10 @@ __global__ __launch_bounds__(256) void commit_kernel(
   const int layer = blockIdx.y;
   const int b = unit / H, h = unit - (unit / H) * H;
   const int a = accept[b];
+  const int off = tree_off[b], end = tree_off[b + 1];
+  const int s = slot[b];
   if (a == -1) return;
   const bool report_here = threadIdx.x == 0 && h == 0 && layer == 0;
-  const int off = tree_off[b], end = tree_off[b + 1];
   const int T = end - off;
   if (off < 0 || end > N || T < 1 || T > kMaxTree) {
     if (report_here) report(err, BOLE_ERR_TREE_SIZE);
@@ -66,75 +48,179 @@ __global__ __launch_bounds__(256) void commit_kernel(
     if (report_here) report(err, BOLE_ERR_BAD_ACCEPT);
     return;
   }
-  const int s = slot[b];
   if (s < 0 || s >= n_slots) {
     if (report_here) report(err, BOLE_ERR_BAD_SLOT);
     return;
   }
-  const float* lp = logP + layer * logp_layer_stride;
-  const float* Ul = Umat + layer * u_layer_stride;
-  const void* kl = DT == BOLE_BF16
-                       ? (const void*)(reinterpret_cast<const uint16_t*>(kmat) + layer * k_layer_stride)
-                       : (const void*)(reinterpret_cast<const float*>(kmat) + layer * k_layer_stride);
-  float* S = state_pool + layer * state_layer_stride + ((int64_t)s * H + h) * d_v * d_k;
-
-  const uint64_t tmask = T == 64 ? ~0ull : ((1ull << T) - 1ull);
-  const uint64_t path = anc[off + a] & tmask;
-  const int La = __popcll(path);
-  const float lpa = lp[(int64_t)(off + a) * H + h];
-  const float Pa = expf(lpa);
-  if (threadIdx.x < kMaxTree && ((path >> threadIdx.x) & 1ull)) {
-    const int t = threadIdx.x;
-    const int p = __popcll(path & ((1ull << t) - 1ull));
-    pj[p] = t;
-    wj[p] = expf(lpa - lp[(int64_t)(off + t) * H + h]);
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kgrp = 8 * (lane >> 4);
-  const int n_mt = d_v >> 4, n_nt = d_k >> 4;
-  const int64_t krow = (int64_t)H * d_k;  // element stride between node rows of k
-  for (int mt = w; mt < n_mt; mt += 4) {
-    const int vrow = 16 * mt + (lane & 15);
-    for (int ng = 0; ng < n_nt; ng += 8) {
-      f32x4 acc[8];
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const float* lp = logP + layer * logp_layer_stride;
+  const float* Ul = Umat + layer * u_layer_stride;
+  float* S = state_pool + layer * state_layer_stride + ((int64_t)s * H + h) * d_v * d_k;
+
+  // transposed path planes: Kt[c][p] (hi[, lo]) and Wt[v][p] (hi, lo), bf16
+  __bf16* Kt_hi = reinterpret_cast<__bf16*>(smem);
+  __bf16* Kt_lo = Kt_hi + d_k * kPRow;
+  __bf16* Wt_hi = Kt_lo + (DT == BOLE_F32 ? d_k * kPRow : 0);
+  __bf16* Wt_lo = Wt_hi + d_v * kPRow;
+
+  // Wave 0 walks the dependent chain (ancestor mask -> gate ratios -> path
+  // rows) while the other waves already stream their slot tiles; a wave's
+  // loads complete in issue order, so the chain must not queue behind them.
+  __shared__ int La_s;
+  __shared__ float Pa_s;
+  // Path rows of one 32-position chunk -> transposed bf16 planes, wave 0 only.
+  // Every load of a batch is issued before the batch is converted and stored,
+  // so a chunk costs one or two memory round trips.
+  auto stage_chunk = [&](int kc, int La) {
+    constexpr int EPK = DT == BOLE_BF16 ? 8 : 4;  // key elements per 16-byte piece
+    const int kp = d_k / EPK, up = d_v >> 2;       // pieces per key row / U row
+    const int per_row = kp + up;
+    const int total = kPathChunk * per_row;
+    constexpr int kBatch = 16;
+    for (int base = 0; base < total; base += 64 * kBatch) {
+      u16x8 buf[kBatch];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kc = 0; kc < La; kc += 32) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int p = kc + kgrp + e;
-          x[e] = p < La ? wj[p] * Ul[((int64_t)(off + pj[p]) * H + h) * d_v + vrow] : 0.0f;
-        }
-        bf16x8 a_hi, a_lo;
-        split_bf16x8(x, a_hi, a_lo);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          if (ng + t < n_nt) {
-            const int c = 16 * (ng + t) + (lane & 15);
-            bf16x8 b_hi, b_lo;
-            load_key8<DT>(kl, krow, pj, kc + kgrp, La, (int64_t)off * krow + (int64_t)h * d_k,
-                          c, b_hi, b_lo);
-            acc[t] = mfma_bf16(a_hi, b_hi, acc[t]);
-            acc[t] = mfma_bf16(a_lo, b_hi, acc[t]);
-            if (DT == BOLE_F32) acc[t] = mfma_bf16(a_hi, b_lo, acc[t]);
+      for (int it = 0; it < kBatch; ++it) {
+        const int id = base + lane + 64 * it;
+        const int p = id / per_row, q = id - (id / per_row) * per_row;
+        const int pg = kc + p;
+        const bool live = id < total && pg < La;
+        const int node = live ? pj[pg] : 0;
+        const int64_t row = (int64_t)(off + node) * H + h;
+        buf[it] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (live) {
+          if (q < kp) {
+            buf[it] = DT == BOLE_BF16
+                          ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(kmat) +
+                                                            layer * k_layer_stride + row * d_k +
+                                                            EPK * q)
+                          : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(kmat) +
+                                                            layer * k_layer_stride + row * d_k +
+                                                            EPK * q);
+          } else {
+            buf[it] = *reinterpret_cast<const u16x8*>(Ul + row * d_v + 4 * (q - kp));
           }
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (ng + t < n_nt) {
-          const int c = 16 * (ng + t) + (lane & 15);
+      for (int it = 0; it < kBatch; ++it) {
+        const int id = base + lane + 64 * it;
+        if (id < total) {
+          const int p = id / per_row, q = id - (id / per_row) * per_row;
+          const int pg = kc + p;
+          if (q < kp) {
+            if (DT == BOLE_BF16) {
+              const bf16x8 kv = __builtin_bit_cast(bf16x8, buf[it]);  // exact bf16 keys
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int vv = 16 * mt + 4 * (lane >> 4) + e;
-            float* ps = S + (int64_t)vv * d_k + c;
-            *ps = Pa * (*ps) + acc[t][e];
+              for (int e = 0; e < 8; ++e) Kt_hi[(EPK * q + e) * kPRow + p] = kv[e];
+            } else {
+              bf16x4 hi, lo;
+              split_bf16x4(__builtin_bit_cast(f32x4, buf[it]), hi, lo);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                Kt_hi[(EPK * q + e) * kPRow + p] = hi[e];
+                Kt_lo[(EPK * q + e) * kPRow + p] = lo[e];
+              }
+            }
+          } else {
+            const int v0 = 4 * (q - kp);
+            const float wgt = pg < La ? wj[pg] : 0.0f;
+            bf16x4 hi, lo;
+            split_bf16x4(__builtin_bit_cast(f32x4, buf[it]) * wgt, hi, lo);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Wt_hi[(v0 + e) * kPRow + p] = hi[e];
+              Wt_lo[(v0 + e) * kPRow + p] = lo[e];
+            }
           }
         }
+      }
+    }
+  };
+  if (w == 0) {
+    const uint64_t tmask = T == 64 ? ~0ull : ((1ull << T) - 1ull);
+    const uint64_t path = anc[off + a] & tmask;
+    const float lpa = lp[(int64_t)(off + a) * H + h];
+    if ((path >> lane) & 1ull) {
+      const int p = __popcll(path & ((1ull << lane) - 1ull));
+      pj[p] = lane;
+      wj[p] = expf(lpa - lp[(int64_t)(off + lane) * H + h]);
+    }
+    if (lane == 0) {
+      La_s = __popcll(path);
+      Pa_s = expf(lpa);
+    }
+    // the wave's own LDS writes are visible to it in program order
+    stage_chunk(0, __popcll(path));
+  }
+
+  // output tiles: value tile nt (16 slot rows) x key tile mt (16 columns), tile
+  // id = nt * n_kt + mt; wave w owns ids w, w + 4, ... in groups of kGroup
+  constexpr int kGroup = 16;
+  const int n_vt = d_v >> 4, n_kt = d_k >> 4, n_tiles = n_vt * n_kt;
+  const int per_wave = (n_tiles + 3) >> 2;
+  const int n_groups = (per_wave + kGroup - 1) / kGroup;  // same for every wave
+  int La = 0;
+  float Pa = 0.0f;
+  for (int grp = 0; grp < n_groups; ++grp) {
+    f32x4 sv[kGroup], acc[kGroup];
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      const int tile = w + 4 * (grp * kGroup + t);
+      acc[t] = zero_f32x4();
+      sv[t] = zero_f32x4();
+      if (tile < n_tiles) {
+        const int nt = tile / n_kt, mt = tile - (tile / n_kt) * n_kt;
+        sv[t] = *reinterpret_cast<const f32x4*>(S + (int64_t)(16 * nt + l16) * d_k + 16 * mt +
+                                                 4 * g4);
+      }
+    }
+    if (grp == 0) {
+      __syncthreads();  // path planes of chunk 0, La, Pa ready
+      La = La_s;
+      Pa = Pa_s;
+    }
+    const int n_chunks = (La + kPathChunk - 1) / kPathChunk;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      // a chunk other than the one left in LDS must be (re)staged
+      if (ch > 0 || (grp > 0 && n_chunks > 1)) {
+        __syncthreads();  // previous chunk fully consumed
+        if (w == 0) stage_chunk(ch * kPathChunk, La);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        const int tile = w + 4 * (grp * kGroup + t);
+        if (tile < n_tiles) {
+          const int nt = tile / n_kt, mt = tile - (tile / n_kt) * n_kt;
+          const bf16x8 ah =
+              *reinterpret_cast<const bf16x8*>(Kt_hi + (16 * mt + l16) * kPRow + 8 * g4);
+          const bf16x8 bh =
+              *reinterpret_cast<const bf16x8*>(Wt_hi + (16 * nt + l16) * kPRow + 8 * g4);
+          const bf16x8 bl =
+              *reinterpret_cast<const bf16x8*>(Wt_lo + (16 * nt + l16) * kPRow + 8 * g4);
+          acc[t] = mfma_bf16(ah, bh, acc[t]);
+          acc[t] = mfma_bf16(ah, bl, acc[t]);
+          if (DT == BOLE_F32) {
+            const bf16x8 al =
+                *reinterpret_cast<const bf16x8*>(Kt_lo + (16 * mt + l16) * kPRow + 8 * g4);
+            acc[t] = mfma_bf16(al, bh, acc[t]);
+          }
+        }
+      }
+    }
+    // D[c][v] of tile (mt, nt): lane holds c = 16mt + 4*g4 + e, v = 16nt + l16
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      const int tile = w + 4 * (grp * kGroup + t);
+      if (tile < n_tiles) {
+        const int nt = tile / n_kt, mt = tile - (tile / n_kt) * n_kt;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = Pa * sv[t][e] + acc[t][e];
+        *reinterpret_cast<f32x4*>(S + (int64_t)(16 * nt + l16) * d_k + 16 * mt + 4 * g4) = o;
       }
     }
   }
@@ -150,13 +236,15 @@ extern "C" int bole_commit_launch(int32_t L, float* state_pool, int64_t state_la
                                   const int32_t* tree_off, const int32_t* accept, int32_t B,
                                   int32_t N, int32_t H, int32_t d_k, int32_t d_v, uint32_t* err,
                                   hipStream_t s) {
-  const dim3 grid(B * H, L), block(256);
+  const dim3 grid(B * H, L), block(bole::kCommitThreads);
+  const size_t planes = (dtype == BOLE_F32 ? 2 : 1) * (size_t)d_k + 2 * (size_t)d_v;
+  const size_t shm = planes * bole::kPRow * sizeof(uint16_t);
   if (dtype == BOLE_BF16)
-    hipLaunchKernelGGL(bole::commit_kernel<BOLE_BF16>, grid, block, 0, s, state_pool,
+    hipLaunchKernelGGL(bole::commit_kernel<BOLE_BF16>, grid, block, shm, s, state_pool,
                        state_layer_stride, n_slots, slot, k, k_layer_stride, U, u_layer_stride,
                        logP, logp_layer_stride, anc, tree_off, accept, B, N, H, d_k, d_v, err);
   else
-    hipLaunchKernelGGL(bole::commit_kernel<BOLE_F32>, grid, block, 0, s, state_pool,
+    hipLaunchKernelGGL(bole::commit_kernel<BOLE_F32>, grid, block, shm, s, state_pool,
                        state_layer_stride, n_slots, slot, k, k_layer_stride, U, u_layer_stride,
                        logP, logp_layer_stride, anc, tree_off, accept, B, N, H, d_k, d_v, err);
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;

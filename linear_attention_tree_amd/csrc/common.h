@@ -9,6 +9,7 @@
 namespace bole {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
@@ -24,6 +25,25 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16.  Lane layout, lane l in [0, 64):
+//   A (16 x 16): lane holds A[l % 16][4*(l/16) .. 4*(l/16)+3]
+//   B (16 x 16): lane holds B[4*(l/16) .. +3][l % 16]
+//   D (16 x 16): lane holds D[4*(l/16) + r][l % 16], r = 0..3
+// D and B coincide, so a product's result feeds the next product's B operand
+// without any data movement.
+__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even split x ~= hi + lo into bf16 parts (relative residual
+// below 2^-16), using packed conversions (two elements per instruction).
+__device__ __forceinline__ void split_bf16x4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+  hi = __builtin_convertvector(x, bf16x4);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), bf16x4);
+}
+
+__device__ __forceinline__ f32x4 zero_f32x4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
 #pragma unroll
@@ -31,15 +51,14 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return z;
 }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
 // Round-to-nearest-even split of 8 floats into bf16 hi + lo parts, x ~= hi + lo
 // (relative residual below 2^-16).
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h = (__bf16)x[e];
-    hi[e] = h;
-    lo[e] = (__bf16)(x[e] - (float)h);
-  }
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  hi = __builtin_convertvector(v, bf16x8);
+  lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
 }
 
 __device__ __forceinline__ void load_f32x8(const float* __restrict__ p, float* x) {
@@ -60,6 +79,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
 
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Local node index read from a caller array, forced into [0, T) so that an
+// inconsistent order/parent array can never address rows outside the tree.
+__device__ __forceinline__ int clamp_node(int x, int T) {
+  return (unsigned)x < (unsigned)T ? x : 0;
 }
 
 // Make a value provably wave-uniform for the compiler (scalar registers).

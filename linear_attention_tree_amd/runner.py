@@ -62,7 +62,8 @@ class TreeRound:
 
     def factor(self, q, k, logP, beta, stream=None):
         t = self.topo
-        bole.bole_factor_gc(q, k, logP, beta, t.anc, t.tree_off, self.G, self.C, self.err, stream)
+        bole.bole_factor_gc(q, k, logP, beta, t.anc, t.order, t.tree_off, self.G, self.C, self.err,
+                            stream)
 
     def verify(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None):
         t = self.topo
@@ -72,14 +73,27 @@ class TreeRound:
             O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
         if U is None:
             U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
-        bole.bole_verify(q, k, v, logP, beta, state_pool, slot, self.G, self.C, t.anc, t.depth,
+        bole.bole_verify(q, k, v, logP, beta, state_pool, slot, self.G, self.C, t.order, t.depth,
                          t.tree_off, t.tree_depth, O, U, self.err, stream)
         return O, U
 
-    def layer(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None):
-        """Factor producer then value-tiled verify for one layer."""
-        self.factor(q, k, logP, beta, stream)
-        return self.verify(q, k, v, logP, beta, state_pool, slot, O, U, stream)
+    def layer(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None,
+              fused=False):
+        """Factor producer then value-tiled verify for one layer (or both in one
+        launch with fused=True)."""
+        if not fused:
+            self.factor(q, k, logP, beta, stream)
+            return self.verify(q, k, v, logP, beta, state_pool, slot, O, U, stream)
+        t = self.topo
+        N, H, _ = q.shape
+        d_v = v.shape[2]
+        if O is None:
+            O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
+        if U is None:
+            U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
+        bole.bole_factor_verify(q, k, v, logP, beta, state_pool, slot, t.anc, t.order, t.depth,
+                                t.tree_off, t.tree_depth, O, U, self.err, stream)
+        return O, U
 
     def commit(self, state_pool, slot, k, U, logP, accept, stream=None):
         t = self.topo

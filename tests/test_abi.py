@@ -33,7 +33,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_symbols()
     assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
-                          "bole_verify", "bole_commit_path", "bole_status_string"}
+                          "bole_verify", "bole_factor_verify", "bole_commit_path",
+                          "bole_status_string"}
     for n in names:
         assert hasattr(L, n), n
         assert hasattr(lat, n), n   # same names in the Python binding
@@ -65,7 +66,7 @@ def test_tree_prep_argument_errors(L):
 
 def test_factor_gc_argument_errors(L):
     f = L.bole_factor_gc
-    args = [FAKE] * 6
+    args = [FAKE] * 7
     assert f(7, *args, 1, 1, 1, 128, FAKE, FAKE, None, None) == E_DTYPE
     assert f(1, None, *args[1:], 1, 1, 1, 128, FAKE, FAKE, None, None) == E_NULL
     assert f(1, *args, 1, 1, 0, 128, FAKE, FAKE, None, None) == E_SHAPE
@@ -86,6 +87,21 @@ def test_verify_argument_errors(L):
     assert _verify(L, n_slots=0) == E_SHAPE
     assert _verify(L, dv=100) == E_UNSUPPORTED
     assert _verify(L, dk=512) == E_UNSUPPORTED
+
+
+def test_factor_verify_argument_errors(L):
+    f = L.bole_factor_verify
+
+    def call(dtype=1, dk=128, dv=128, O=FAKE, B=1):
+        return f(dtype, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 B, 1, 1, dk, dv, O, FAKE, None, None)
+
+    assert call(dtype=9) == E_DTYPE
+    assert call(O=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(dk=256) == E_UNSUPPORTED          # one staged chunk only
+    assert call(dtype=0, dk=128) == E_UNSUPPORTED
+    assert call(dtype=0, dk=64, dv=24) == E_UNSUPPORTED
 
 
 def test_commit_argument_errors(L):

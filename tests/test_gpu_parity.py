@@ -151,8 +151,13 @@ def test_factor_gc_against_definition(cases, name):
         for h in range(case.cfg.H):
             P, G, C, d = tree_factors(par, x.q64[o:o + T, h], x.k64[o:o + T, h],
                                       x.g64[o:o + T, h], x.beta64[o:o + T, h])
+            lev = out["order"][o:o + T]          # level position -> local node
             Gg = out["G"][b, h]
             Cg = out["C"][b, h]
+            G = G[np.ix_(lev, lev)]
+            C = C[np.ix_(lev, lev)]
+            # level order is parent-before-child: G strictly lower, C lower triangular
+            assert np.all(np.triu(Gg[:T, :T]) == 0) and np.all(np.triu(Cg[:T, :T], 1) == 0)
             # exact zeros outside the ancestor mask and the padding
             assert np.all(Gg[T:] == 0) and np.all(Gg[:, T:] == 0)
             assert np.all(Cg[T:] == 0) and np.all(Cg[:, T:] == 0)
@@ -302,3 +307,31 @@ def test_bad_slot_and_accept_bits():
     torch.cuda.synchronize()
     assert rnd.error_bits() == oracle.ERR_BAD_ACCEPT
     assert torch.equal(pool, before)
+
+
+# ---------------------------------------------------------------------------
+# fused factor + verify
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "batched", "ragged", "target"])
+def test_factor_verify_bit_identical_to_two_calls(cases, name):
+    """One-launch factor+verify gives exactly the bits of factor_gc then verify."""
+    from linear_attention_tree_amd import TreeRound
+    from helpers import to_dev
+    case = get_case(cases, name, n_layers=1)
+    f = case.forest
+    say(f"factor_verify vs two calls {name}")
+    d = to_dev(case, 0)
+    rnd = TreeRound(f.parent, f.tree_off, case.cfg.H)
+    logP = rnd.prep(d["g"][None])[0]
+    pool = torch.from_numpy(case.S_pre[0]).cuda()
+    slot = torch.from_numpy(case.slot).cuda()
+    O1, U1 = rnd.layer(d["q"], d["k"], d["v"], logP, d["beta"], pool, slot)
+    O2, U2 = rnd.layer(d["q"], d["k"], d["v"], logP, d["beta"], pool, slot, fused=True)
+    torch.cuda.synchronize()
+    assert rnd.error_bits() == 0
+    assert torch.equal(O1, O2) and torch.equal(U1, U2)
+    O, U, _ = oracle_layer(case, 0, accept=False)
+    eo = block_rel_err(O2.float().cpu().numpy(), O, f.tree_off)
+    eu = block_rel_err(U2.cpu().numpy(), U, f.tree_off)
+    say(f"  fused O {eo:.2e}  U {eu:.2e}")
+    assert eo <= tolerance(case.cfg) and eu <= tolerance(case.cfg)
