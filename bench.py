@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--path", default="fused", choices=sorted(STEPS),
                     help="fused: prep + factor_verify + commit; split: the four calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -228,6 +230,14 @@ def main():
     cfg = W.CONFIGS[args.config]
     if cfg.L != 1:
         cfg = W.Config(**{**cfg.__dict__, "L": 1})
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     sets = [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(args.sets)]
     e = 2 if cfg.dtype == "bf16" else 4
 

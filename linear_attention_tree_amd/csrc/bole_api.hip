@@ -120,7 +120,7 @@ int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, i
   if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
   if (!state_pool || !slot || !k || !U || !logP || !anc || !tree_off || !accept)
     return BOLE_E_NULL;
-  if (L < 1 || L > 65535 || B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 1))
+  if (L < 1 || L > 65535 || B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 16))
     return BOLE_E_SHAPE;
   if (state_layer_stride < 0 || k_layer_stride < 0 || u_layer_stride < 0 ||
       logp_layer_stride < 0)

@@ -43,18 +43,34 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(
     return;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // wave 0's parent loads go out first: the topology chain starts from them
+  int p = -1;
+  if (w == 0) p = parent[off + min(lane, T - 1)];
   // gate values of this block's columns (independent of the topology)
   const int c = threadIdx.x & (kGateCols - 1);
   const int lh = blockIdx.y * kGateCols + c;
   const bool col_ok = g != nullptr && lh < L * H;
   const int l = col_ok ? lh / H : 0, h = col_ok ? lh - (lh / H) * H : 0;
   const int64_t base = (int64_t)l * N * H + h;
-  if (col_ok)
-    for (int i = w; i < T; i += kPrepThreads / 64) val[i][c] = g[base + (int64_t)(off + i) * H];
+  // every gate load is issued before the first is stored: node T-1 stands in
+  // for slots past the tree and column (0, 0) for columns past L*H, neither of
+  // which is stored
+  if (g != nullptr) {  // uniform
+    constexpr int kPer = kMaxTree / (kPrepThreads / 64);
+    const float* gcol = g + base + (int64_t)off * H;  // node i at gcol[i * H]
+    float gv[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) gv[r] = gcol[min(w + (kPrepThreads / 64) * r, T - 1) * H];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = w + (kPrepThreads / 64) * r;
+      if (col_ok && i < T) val[i][c] = gv[r];
+    }
+  }
 
   if (w == 0) {
     const bool live = lane < T;
-    const int p = live ? parent[off + lane] : -1;
+    p = live ? p : -1;
     const bool bad = live && p != -1 && (p < 0 || p >= T || p == lane);
     uint32_t fail = 0;
     int dmax = 0;
@@ -123,8 +139,10 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(
     }
     __syncthreads();
   }
-  if (col_ok)
-    for (int i = w; i < T; i += kPrepThreads / 64) logP[base + (int64_t)(off + i) * H] = val[i][c];
+  if (col_ok) {
+    float* lcol = logP + base + (int64_t)off * H;
+    for (int i = w; i < T; i += kPrepThreads / 64) lcol[i * H] = val[i][c];
+  }
 }
 
 }  // namespace bole

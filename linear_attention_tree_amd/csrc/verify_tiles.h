@@ -1,0 +1,154 @@
+// Tile geometry and fragment helpers shared by the verify kernels of libbole.
+#pragma once
+
+#include "common.h"
+
+namespace bole {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBV = 16 * kWaves;  // value columns per workgroup
+
+template <int DT>
+struct StageCfg {
+  static constexpr int KC = DT == BOLE_BF16 ? 128 : 64;  // d_k chunk staged per pass
+  static constexpr int LROW = KC;                         // bf16 per LDS row
+  static constexpr int CHUNKS = KC / 8;                   // 16-byte chunks per row
+  static constexpr int NMAT = DT == BOLE_BF16 ? 2 : 4;    // Q, K (hi) [+ Q, K lo]
+};
+
+// XOR swizzle of 16-byte chunks within a staged row: the 16 rows an A fragment
+// reads at one K offset land in 16 different bank groups.
+template <int DT>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ (row & (StageCfg<DT>::CHUNKS - 1));
+}
+
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void* base, int64_t elem) {
+  if (DT == BOLE_BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(base)[elem]);
+  return reinterpret_cast<const float*>(base)[elem];
+}
+
+template <int DT>
+__device__ __forceinline__ void store_scalar(void* base, int64_t elem, float x) {
+  if (DT == BOLE_BF16)
+    reinterpret_cast<uint16_t*>(base)[elem] = float_to_bf16_bits(x);
+  else
+    reinterpret_cast<float*>(base)[elem] = x;
+}
+
+// Stage one d_k chunk of the tree's Q and K rows (level order) into LDS as bf16
+// (float32 rows are split into hi and lo planes).  All loads are issued before
+// the first LDS store so one memory round trip covers the whole chunk.
+template <int DT>
+__device__ __forceinline__ void stage_qk(__bf16* stage, const void* q, const void* k,
+                                         const int* rowNode, int T, int off, int H, int h,
+                                         int d_k, int kc0) {
+  using SC = StageCfg<DT>;
+  constexpr int EPP = DT == BOLE_BF16 ? 8 : 4;       // elements per 16-byte global piece
+  constexpr int PIECES = SC::KC / EPP;                // pieces per row
+  constexpr int TOTAL = 2 * kMaxTree * PIECES;        // Q and K
+  constexpr int PER = TOTAL / kThreads;
+  u16x8 buf[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int id = threadIdx.x + kThreads * it;
+    const int mat = id / (kMaxTree * PIECES);
+    const int rem = id - mat * (kMaxTree * PIECES);
+    const int row = rem / PIECES, pc = rem - (rem / PIECES) * PIECES;
+    const int kk = kc0 + EPP * pc;
+    u16x8 val = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < T && kk < d_k) {
+      const int64_t e = ((int64_t)(off + rowNode[row]) * H + h) * d_k + kk;
+      val = DT == BOLE_BF16
+                ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat == 0 ? q : k) + e)
+                : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(mat == 0 ? q : k) + e);
+    }
+    buf[it] = val;
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int id = threadIdx.x + kThreads * it;
+    const int mat = id / (kMaxTree * PIECES);
+    const int rem = id - mat * (kMaxTree * PIECES);
+    const int row = rem / PIECES, pc = rem - (rem / PIECES) * PIECES;
+    if (DT == BOLE_BF16) {
+      *reinterpret_cast<u16x8*>(stage + (mat * kMaxTree + row) * SC::LROW + 8 * swz<DT>(row, pc)) =
+          buf[it];
+    } else {
+      const f32x4 x = __builtin_bit_cast(f32x4, buf[it]);
+      bf16x4 hi, lo;
+      split_bf16x4(x, hi, lo);
+      // 4 elements = half a 16-byte chunk
+      const int ch = swz<DT>(row, pc >> 1), half = pc & 1;
+      *reinterpret_cast<bf16x4*>(stage + (mat * kMaxTree + row) * SC::LROW + 8 * ch + 4 * half) = hi;
+      *reinterpret_cast<bf16x4*>(stage + ((2 + mat) * kMaxTree + row) * SC::LROW + 8 * ch +
+                                 4 * half) = lo;
+    }
+  }
+}
+
+// G and C are parked in LDS already split into bf16 hi/lo planes (G negated),
+// each plane 64 rows x 64 entries, laid out for the A fragments of
+// v_mfma_f32_16x16x32_bf16 with a permuted K order: the 32 K positions of block
+// (I, J) cover the two 16-row tiles 2J and 2J+1, and lane l's eight positions
+// 8*(l/16) + e map to row 4*(l/16) + (e & 3) of tile 2J + (e >> 2).  With that
+// order a lane's B fragment is just its own accumulator entries of tiles 2J and
+// 2J+1 (16x16 accumulator layout: rows 4*(l/16) .. +3 of column l%16), so the
+// recursion never moves Z or U between lanes.  Within a row, the 16-byte chunk
+// (J, l/16) holding a fragment is XOR-swizzled so 16 rows hit distinct banks.
+// Blocks: (I, J) with J <= I/2, index kBlk(I, J) in {0..5}.
+constexpr int kGcPlane = kMaxTree * kMaxTree;  // bf16 per plane
+
+__device__ __forceinline__ int gc_pos(int row, int col) {
+  const int J = col >> 5, c32 = col & 31;
+  const int chunk = (J << 2) | ((c32 & 15) >> 2);
+  const int phys = chunk ^ ((row >> 1) & 7);
+  return row * kMaxTree + phys * 8 + ((c32 >> 4) << 2) + (c32 & 3);
+}
+
+__device__ __forceinline__ int gc_frag(int row, int J, int g) {
+  return row * kMaxTree + (((J << 2) | g) ^ ((row >> 1) & 7)) * 8;
+}
+
+__device__ __forceinline__ constexpr int kBlk(int I, int J) { return I < 2 ? I : 2 + 2 * (I - 2) + J; }
+
+__device__ __forceinline__ void load_tri_blocks(const __bf16* hi_plane, const __bf16* lo_plane,
+                                                int nmt, int lane, bf16x8* hi, bf16x8* lo) {
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J <= I / 2; ++J) {
+      const int idx = kBlk(I, J);
+      if (I < nmt) {
+        const int o = gc_frag(16 * I + l16, J, g);
+        hi[idx] = *reinterpret_cast<const bf16x8*>(hi_plane + o);
+        lo[idx] = *reinterpret_cast<const bf16x8*>(lo_plane + o);
+      } else {
+        hi[idx] = zero_bf16x8();
+        lo[idx] = zero_bf16x8();
+      }
+    }
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& a, const f32x4& b) {
+  const f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ void split_pair(const f32x4& a, const f32x4& b, bf16x8& hi,
+                                           bf16x8& lo) {
+  const f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  hi = __builtin_convertvector(v, bf16x8);
+  lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
+}
+
+// Gram tiles (I >= J) computed in the fused variant; job j of a workgroup is
+// tile kTileI/J[j >> 1] of K K^T (j even, for G) or Q K^T (j odd, for C).
+__constant__ constexpr int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ constexpr int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+constexpr int kJobsPerWave = (20 + kWaves - 1) / kWaves;
+
+}  // namespace bole
