@@ -26,10 +26,6 @@ constexpr int kCommitBlk = 64;    // slot rows / columns per wave
 constexpr int kCommitTiles = 4;   // 16-wide tiles per block side
 constexpr int kPathChunk = 32;    // path positions per MFMA K step
 
-// all-ones or zero: a mask applied to a loaded value (a select would let the
-// compiler move the load behind a branch and wait for it there)
-__device__ __forceinline__ uint32_t keep(bool b) { return 0u - (uint32_t)b; }
-
 template <int DT>
 __global__ __launch_bounds__(64) void commit_kernel(
     float* __restrict__ state_pool, int64_t state_layer_stride, int32_t n_slots,

@@ -105,6 +105,18 @@ __device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
 // Workgroup-id remap so that consecutive logical ids land on the same XCD.
 // MI355X dispatches workgroup w to XCD (w mod 8); this returns the logical id
 // whose XCD-local rank is w / 8, with XCD x owning a contiguous logical range.
+// Gate ratio P_i / P_j = exp(logP_i - logP_j) from the sums prescaled to base 2
+// (e2 = logP * log2(e), one rounding), as one hardware exp2.  Relative error
+// about |logP| * 2^-24, against 1 ulp for expf; it feeds float32 products.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float gate_ratio(float e2_i, float e2_j) {
+  return __builtin_amdgcn_exp2f(e2_i - e2_j);
+}
+
+// all-ones or zero: a mask applied to a loaded value (a select would let the
+// compiler move the load behind a branch and wait for it there)
+__device__ __forceinline__ uint32_t keep(bool b) { return 0u - (uint32_t)b; }
+
 __device__ __forceinline__ int xcd_remap(int w, int total) {
   constexpr int kXcd = 8;
   const int x = w % kXcd, k = w / kXcd;

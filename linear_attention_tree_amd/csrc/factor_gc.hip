@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kGcThreads) void factor_gc_kernel(
   using SC = GcStage<DT>;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::KC];
   __shared__ int rowNode[kMaxTree];
-  __shared__ float rowLogP[kMaxTree];
+  __shared__ int posOf[kMaxTree];  // local node id -> level position
+  __shared__ __align__(16) float rowE2[kMaxTree];
 
   const int unit = xcd_remap(blockIdx.x, B * H);
   const int b = unit / H, h = unit - (unit / H) * H;
@@ -56,23 +57,42 @@ __global__ __launch_bounds__(kGcThreads) void factor_gc_kernel(
     if (threadIdx.x == 0 && h == 0) report(err, BOLE_ERR_TREE_SIZE);
     return;
   }
-  if (threadIdx.x < kMaxTree) rowNode[threadIdx.x] = lane < T ? clamp_node(order[off + lane], T) : 0;
+  const int ord = order[off + min(lane, T - 1)];
+  const int node_l = lane < T ? clamp_node(ord, T) : 0;
+  if (threadIdx.x < kMaxTree) {
+    rowNode[threadIdx.x] = node_l;
+    if (lane < T) posOf[node_l] = lane;
+  }
   __syncthreads();
 
-  // epilogue operands (small, issued before the staging loads are waited on)
-  uint64_t ai[4];
-  float lpi[4], bi[4], lpj[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 16 * w + 4 * g4 + r;
-    const int ni = rowNode[i];
-    const bool iv = i < T;
-    ai[r] = iv ? anc[off + ni] : 0ull;
-    lpi[r] = iv ? logP[(int64_t)(off + ni) * H + h] : 0.0f;
-    bi[r] = iv ? beta[(int64_t)(off + ni) * H + h] : 0.0f;
+  // The products are taken transposed (key rows of column tile nt as the M
+  // operand), so a lane holds row i = 16w + l16 at the four consecutive columns
+  // 16nt + 4g .. +3: one float4 store per tile and matrix.  Operand order,
+  // accumulation order and epilogue arithmetic are those of the fused factor +
+  // verify kernel, which makes the two paths' G and C bit-identical.
+  const int i = 16 * w + l16;
+  const bool iv = i < T;
+  const int ni = rowNode[i];
+  // epilogue operands of the lane's row: unconditional loads (ni is a valid
+  // node), issued before the staging loads are waited on
+  const uint64_t an_raw = anc[off + ni];
+  const float lp_raw = logP[(int64_t)(off + ni) * H + h];
+  const float bt_raw = beta[(int64_t)(off + ni) * H + h];
+  const float e2i = lp_raw * kLog2e;
+  const float bi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & keep(iv));
+  if (g4 == 0)
+    rowE2[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, e2i) & keep(iv));
+  // the row's ancestor mask moved from node ids to level positions, where four
+  // consecutive columns are four consecutive bits
+  uint64_t apos = 0ull;
+  {
+    uint64_t m = an_raw & (T == 64 ? ~0ull : ((1ull << T) - 1ull));
+    while (m) {
+      apos |= 1ull << posOf[__builtin_ctzll(m)];
+      m &= m - 1ull;
+    }
+    apos &= 0ull - (uint64_t)iv;
   }
-  if (threadIdx.x < kMaxTree)
-    rowLogP[threadIdx.x] = lane < T ? logP[(int64_t)(off + rowNode[lane]) * H + h] : 0.0f;
 
   f32x4 qk[4], kk[4];
 #pragma unroll
@@ -95,14 +115,16 @@ __global__ __launch_bounds__(kGcThreads) void factor_gc_kernel(
       const int rem = id - mat * (kMaxTree * PIECES);
       const int row = rem / PIECES, pc = rem - (rem / PIECES) * PIECES;
       const int kk2 = kc0 + EPP * pc;
-      u16x8 val = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < T && kk2 < d_k) {
-        const int64_t e = ((int64_t)(off + rowNode[row]) * H + h) * d_k + kk2;
-        val = DT == BOLE_BF16
-                  ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat ? k : q) + e)
-                  : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(mat ? k : q) + e);
-      }
-      buf[it] = val;
+      // unconditional load (row and column clamped into the tree), zeroed after
+      const bool in = row < T && kk2 < d_k;
+      const int64_t e =
+          ((int64_t)(off + rowNode[min(row, T - 1)]) * H + h) * d_k + (kk2 < d_k ? kk2 : 0);
+      const u16x8 val =
+          DT == BOLE_BF16
+              ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat ? k : q) + e)
+              : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(mat ? k : q) + e);
+      const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      buf[it] = in ? val : zero;
     }
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
@@ -127,28 +149,27 @@ __global__ __launch_bounds__(kGcThreads) void factor_gc_kernel(
 #pragma unroll
       for (int kk2 = 0; kk2 < SC::KC / 32; ++kk2) {
         if (kc0 + 32 * kk2 < d_k) {
-          const int arow = 16 * w + l16;
-          const int ao = arow * SC::KC + 8 * gc_swz<DT>(arow, 4 * kk2 + g4);
+          const int ao = i * SC::KC + 8 * gc_swz<DT>(i, 4 * kk2 + g4);
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(stage + ao);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::KC + ao);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
-            if (nt < nmt) {
+            if (nt < nmt && nt <= w) {
               const int brow = 16 * nt + l16;
               const int bo = (kMaxTree + brow) * SC::KC + 8 * gc_swz<DT>(brow, 4 * kk2 + g4);
               const bf16x8 bk = *reinterpret_cast<const bf16x8*>(stage + bo);
-              qk[nt] = mfma_bf16(aq, bk, qk[nt]);
-              kk[nt] = mfma_bf16(ak, bk, kk[nt]);
+              qk[nt] = mfma_bf16(bk, aq, qk[nt]);
+              kk[nt] = mfma_bf16(bk, ak, kk[nt]);
               if (DT == BOLE_F32) {
                 const int lo_off = 2 * kMaxTree * SC::KC;
                 const bf16x8 aql = *reinterpret_cast<const bf16x8*>(stage + lo_off + ao);
                 const bf16x8 akl =
                     *reinterpret_cast<const bf16x8*>(stage + lo_off + kMaxTree * SC::KC + ao);
                 const bf16x8 bkl = *reinterpret_cast<const bf16x8*>(stage + lo_off + bo);
-                qk[nt] = mfma_bf16(aq, bkl, qk[nt]);
-                qk[nt] = mfma_bf16(aql, bk, qk[nt]);
-                kk[nt] = mfma_bf16(ak, bkl, kk[nt]);
-                kk[nt] = mfma_bf16(akl, bk, kk[nt]);
+                qk[nt] = mfma_bf16(bkl, aq, qk[nt]);
+                qk[nt] = mfma_bf16(bk, aql, qk[nt]);
+                kk[nt] = mfma_bf16(bkl, ak, kk[nt]);
+                kk[nt] = mfma_bf16(bk, akl, kk[nt]);
               }
             }
           }
@@ -156,26 +177,25 @@ __global__ __launch_bounds__(kGcThreads) void factor_gc_kernel(
       }
     }
   }
-  // epilogue: lane holds rows 16w + 4*(lane/16) + r, column 16nt + lane%16 (level
-  // positions); the mask test is on the nodes those positions hold
+  // epilogue, branch-free: every entry is computed and the mask clears the ones
+  // outside it (an overflowing ratio there is cleared too)
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) lpj[nt] = rowLogP[16 * nt + l16];
+  for (int nt = 0; nt < 4; ++nt) {
+    const int j0 = 16 * nt + 4 * g4;
+    const uint32_t m4 = (uint32_t)(apos >> j0) & 15u;
+    const uint32_t d = (uint32_t)(i - j0);
+    const uint32_t m4g = m4 & ~(d < 4u ? 1u << d : 0u);  // G has no diagonal
+    const f32x4 e2j = *reinterpret_cast<const f32x4*>(rowE2 + j0);
+    f32x4 gv, cv;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 16 * w + 4 * g4 + r;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = 16 * nt + l16;
-      const int nj = rowNode[j];
-      float gv = 0.0f, cv = 0.0f;
-      if (i < T && j < T && ((ai[r] >> nj) & 1ull)) {
-        const float ratio = expf(lpi[r] - lpj[nt]);
-        cv = ratio * qk[nt][r];
-        if (j != i) gv = bi[r] * ratio * kk[nt][r];
-      }
-      Gt[i * kMaxTree + j] = gv;
-      Ct[i * kMaxTree + j] = cv;
+    for (int e = 0; e < 4; ++e) {
+      const float c1 = gate_ratio(e2i, e2j[e]) * qk[nt][e];
+      const float g1 = bi * gate_ratio(e2i, e2j[e]) * kk[nt][e];
+      cv[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c1) & keep((m4 >> e) & 1u));
+      gv[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, g1) & keep((m4g >> e) & 1u));
     }
+    *reinterpret_cast<f32x4*>(Gt + i * kMaxTree + j0) = gv;
+    *reinterpret_cast<f32x4*>(Ct + i * kMaxTree + j0) = cv;
   }
 }
 

@@ -1,30 +1,34 @@
 // Value-tiled closed-form verification (Bole, arXiv page section IV-B; the
-// review's Eqs. 7 and 8).  One workgroup per (tree b, head h, value tile r) of
-// kBV value columns; the tree is never split across workgroups.  Each of the
-// eight waves owns 16 value columns and every node row, so after the operands
-// are staged no wave ever waits for another.  At d_v = 128 a head is one
-// workgroup and the whole forest fits on the chip in a single round.
+// review's Theorem 1 and Eqs. 6-8).  One workgroup per (tree b, head h, value
+// tile r) of kBV value columns; the tree is never split across workgroups.  At
+// d_v = 128 a head is one workgroup and the whole forest fits on the chip in a
+// single round.
 //
 // Rows are taken in level order (nodes sorted by depth, the order produced by
 // tree preparation).  That is a parent-before-child indexing, so G is strictly
-// lower triangular and C lower triangular (arXiv page, Theorem 1 discussion),
-// and the rows of depth < m form a prefix that Z^(m) = (-G)^m R leaves at
-// exactly zero (Lemma 3).  The kernel skips every 16x16 tile that structure
-// makes zero.
+// lower triangular and C lower triangular (arXiv page, Theorem 1 discussion).
 //
+// The structured system (I + G) U = R is solved by forward substitution over
+// the four 16-row tiles, which the pages allow (the closed form fixes the
+// outputs, not how the system is solved).  Each diagonal block's inverse is the
+// finite Neumann series of Eq. 8 restricted to the tile; it depends on Q, K,
+// beta and the gates only, so it is formed while the state slice is in flight.
+//
+//  Gram     (fused variant) Q K^T and K K^T from the staged rows, masked
+//           epilogue, into bf16 hi/lo planes of -G and C in LDS.
+//  Diag     waves 0-3: (I + G_tt)^-1 for tile t by repeated squaring.
 //  Phase A  [Q;K] S_pre^(r) on v_mfma_f32_16x16x32_bf16: Q/K rows staged once
-//           in LDS (level order), S_pre rows of the wave's columns loaded
-//           straight into B fragments and split into bf16 hi+lo (float32 Q/K
-//           are split too), float32 accumulation.
-//           B0 = D_P QS and R = D_beta (V - D_P KS) in the accumulators.
-//  Phase C  finite Neumann recursion of Eq. 8 on v_mfma_f32_16x16x32_bf16:
-//           Z <- -G Z, U += Z for d_b steps.  With a permuted K order (see
-//           load_tri_blocks) the B operand of a product is the lane's own
-//           accumulator entries of two Z tiles, so Z and U never leave
-//           registers.  G and Z are split into bf16 hi+lo, three products per
-//           block (hi.hi + lo.hi + hi.lo), float32 accumulation.
-//  Phase D  readout O = B0 + C U the same way; O (token dtype) and the compact
-//           float32 U are written back to the nodes' rows.
+//           in LDS (level order), S_pre rows of the wave's 16 value columns
+//           loaded straight into B fragments and split into bf16 hi+lo
+//           (float32 Q/K split too).  B0 = D_P QS, R = D_beta (V - D_P KS).
+//  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
+//           a permuted K order (load_tri_blocks) that makes the lane's own U
+//           tiles the B operand: U never leaves registers.
+//  Readout  O = B0 + C U; O (token dtype) and the compact float32 U are written
+//           back to the nodes' rows.  Every operand is split hi + lo, float32
+//           accumulation.
+#include <type_traits>
+
 #include "verify_tiles.h"
 
 namespace bole {
@@ -32,8 +36,9 @@ namespace bole {
 // FUSED = false: G and C come from bole_factor_gc.  FUSED = true: the Gram
 // products and their masked epilogue run here, from the Q/K rows already staged
 // for the state contractions, with the same arithmetic as bole_factor_gc (d_k
-// must fit one staged chunk).
-template <int DT, bool FUSED>
+// must fit one staged chunk).  ONE: d_k fits one staged chunk (always so when
+// fused), which drops the re-staging loop and its registers.
+template <int DT, bool FUSED, bool ONE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ logP, const float* __restrict__ beta,
@@ -45,11 +50,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     int32_t d_v, void* __restrict__ O, float* __restrict__ U, uint32_t* __restrict__ err) {
   using SC = StageCfg<DT>;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::LROW];
-  __shared__ __align__(16) __bf16 gcs[4 * kGcPlane];  // -G hi, -G lo, C hi, C lo
-  __shared__ float rowP[kMaxTree], rowBeta[kMaxTree], rowLogP[kMaxTree];
-  __shared__ uint64_t rowAnc[kMaxTree];
-  __shared__ int rowNode[kMaxTree];
-  static_assert(sizeof(stage) >= kWaves * 4 * 64 * sizeof(f32x4), "B0 parking space");
+  // planes: -G hi, -G lo, C hi, C lo
+  __shared__ __align__(16) __bf16 gcs[4 * kGcPlane];
+  __shared__ __align__(16) float rowP[kMaxTree], rowBeta[kMaxTree], rowE2[kMaxTree];
+  __shared__ uint64_t rowApos[kMaxTree];  // ancestor-or-self set in level positions
+  __shared__ int posOf[kMaxTree];         // local node id -> level position
+  __shared__ int rowDep[kMaxTree];
+  __shared__ __align__(16) int rowNode[kMaxTree];
+  __shared__ bf16x4 invs[4][2][64];  // (I + G_tt)^-1, A layout, hi / lo
 
   const int NV = (d_v + kBV - 1) / kBV;
   const int lid = xcd_remap(blockIdx.x, B * H * NV);
@@ -59,6 +67,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave id, uniform
   const int g4 = lane >> 4, l16 = lane & 15;
 
+  // independent per-tree scalars, fetched together
+  const int off = tree_off[b], end = tree_off[b + 1];
+  const int td = tree_depth[b];
+  const int s = slot[b];
+  const int T = end - off;
+  if (off < 0 || end > N || T < 1 || T > kMaxTree) {
+    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_TREE_SIZE);
+    return;
+  }
+  if (td < 0) return;  // rejected by tree preparation
+  if (s < 0 || s >= n_slots) {
+    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_BAD_SLOT);
+    return;
+  }
+  const int nmt = (T + 15) >> 4;
+
+  // Every global load below is unconditional (indices are clamped into the
+  // tree and values masked afterwards): a load behind a divergent branch makes
+  // the wait for it conservative, and it would then wait for every load issued
+  // after it as well.
+  // level-order rows: row p holds node order[p]
+  const int ord = order[off + min(lane, T - 1)];
   // G and C depend on the unit only: their loads go out first and are parked in
   // LDS once the operands below are in flight.  The fused variant clears the
   // planes instead (tiles above the diagonal are read and must be zero).
@@ -80,39 +110,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
           u16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  // independent per-tree scalars, fetched together
-  const int off = tree_off[b], end = tree_off[b + 1];
-  const int td = tree_depth[b];
-  const int s = slot[b];
-  const int T = end - off;
-  if (off < 0 || end > N || T < 1 || T > kMaxTree) {
-    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_TREE_SIZE);
-    return;
+  const int node_l = lane < T ? clamp_node(ord, T) : 0;
+  if (threadIdx.x < kMaxTree) {
+    rowNode[threadIdx.x] = node_l;
+    if (lane < T) posOf[node_l] = lane;
   }
-  if (td < 0) return;  // rejected by tree preparation
-  if (s < 0 || s >= n_slots) {
-    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_BAD_SLOT);
-    return;
-  }
-  const int d_b = min(td, T - 1);
-  const int nmt = (T + 15) >> 4;
-
-  // level-order rows: row p holds node order[p]
-  const int node_l = lane < T ? clamp_node(order[off + lane], T) : 0;
-  if (threadIdx.x < kMaxTree) rowNode[threadIdx.x] = node_l;
   __syncthreads();  // rowNode visible
 
-  // everything below depends on the rows only: one round trip for all operands
-  // depth of level-order row `lane` (nondecreasing in the row index)
-  const int dep_row = lane < T ? depth[off + node_l] : 0x7fff;
-  float lp_l = 0.0f, bt_l = 0.0f;
-  uint64_t an_l = 0ull;
-  if (threadIdx.x < kMaxTree && lane < T) {
-    const int64_t tok = (int64_t)(off + node_l) * H + h;
-    lp_l = logP[tok];
-    bt_l = beta[tok];
-    if (FUSED) an_l = anc[off + node_l];
-  }
+  // everything below depends on the rows only.  Issue order: row scalars, the
+  // Q/K rows (needed first), then the state slice, which is consumed last.
+  const int64_t tok_l = (int64_t)(off + node_l) * H + h;
+  const int dep_raw = depth[off + node_l];
+  const float lp_raw = logP[tok_l];
+  const float bt_raw = beta[tok_l];
+  const uint64_t an_raw = FUSED ? anc[off + node_l] : 0ull;
+  u16x8 qkbuf[QkCfg<DT>::PER];
+  qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, 0);
 
   // S_pre rows of this wave's 16 value columns: first chunk's B fragments
   const int vloc = 16 * w + l16;
@@ -120,31 +133,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const bool vin = vcol < d_v;
   const float* Srow = state_pool + (((int64_t)s * H + h) * d_v + (vin ? vcol : 0)) * d_k;
   float sx[SC::KC / 32][8];
+  // K positions past d_k read the row's first entries instead: they meet staged
+  // Q/K columns that are zero.  Lanes past d_v compute columns never stored.
   auto load_s = [&](int kc0) {
 #pragma unroll
     for (int kk = 0; kk < SC::KC / 32; ++kk) {
       const int kidx = kc0 + 32 * kk + 8 * g4;
-      if (vin && kidx < d_k) {
-        load_f32x8(Srow + kidx, sx[kk]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sx[kk][e] = 0.0f;
-      }
+      load_f32x8(Srow + (kidx < d_k ? kidx : 0), sx[kk]);
     }
   };
   load_s(0);
-
-  // this lane's V entries (accumulator layout), consumed after phase A
-  float vv[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int p = 16 * mt + 4 * g4 + e;
-      vv[mt][e] = (mt < nmt && p < T && vin)
-                      ? load_scalar<DT>(v, ((int64_t)(off + rowNode[p]) * H + h) * d_v + vcol)
-                      : 0.0f;
-    }
+  // nothing that waits on a load may be scheduled above this point: every
+  // load of the prologue is in flight before the first wait
+  __builtin_amdgcn_sched_barrier(0);
 
   // park G (negated) and C in LDS, split once into bf16 hi/lo planes
 #pragma unroll
@@ -158,11 +159,175 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat) * kGcPlane + o) = hi;
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat + 1) * kGcPlane + o) = lo;
   }
-  if (threadIdx.x < kMaxTree) {
-    rowP[threadIdx.x] = lane < T ? expf(lp_l) : 0.0f;
-    rowBeta[threadIdx.x] = bt_l;
-    rowLogP[threadIdx.x] = lp_l;
-    rowAnc[threadIdx.x] = an_l;
+  // depth of level-order row `lane` (nondecreasing in the row index)
+  const bool row_in = lane < T;
+  const int dep_row = row_in ? dep_raw : 0x7fff;
+  // every wave writes the same row tables, and rows past the tree are cleared
+  // by masks, not selects: no branch for the loads to sink into
+  const uint32_t rk = keep(row_in);
+  rowP[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, expf(lp_raw)) & rk);
+  rowBeta[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & rk);
+  rowE2[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, lp_raw * kLog2e) & rk);
+  if (FUSED) {
+    // the row's ancestor mask moved from node ids to level positions, where
+    // four consecutive columns are four consecutive bits
+    uint64_t m = an_raw & (T == 64 ? ~0ull : ((1ull << T) - 1ull)), apos = 0ull;
+    while (m) {
+      apos |= 1ull << posOf[__builtin_ctzll(m)];
+      m &= m - 1ull;
+    }
+    rowApos[lane] = apos & (0ull - (uint64_t)row_in);
+  }
+  rowDep[lane] = dep_row;
+  qk_commit<DT>(stage, qkbuf);  // waits for the Q/K rows (and row scalars) only
+  using VRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
+  VRaw vraw[4][4];
+  {
+    // this lane's V entries (accumulator layout), consumed after phase A and
+    // issued once the Q/K rows are in (so they do not delay them).  Rows past
+    // the tree read row T-1 and a column past d_v reads column 0; the values
+    // are masked when used.
+    const VRaw* vcolp = reinterpret_cast<const VRaw*>(v) + (int64_t)h * d_v + (vin ? vcol : 0);
+    const int64_t vstride = (int64_t)H * d_v;  // elements between node rows
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = min(16 * mt + 4 * g4 + e, T - 1);
+        vraw[mt][e] = vcolp[(int64_t)(off + rowNode[p]) * vstride];
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // staged rows and row tables visible
+
+  if (FUSED) {
+    // d_k fits one staged chunk (checked by the host): each Gram tile is
+    // finished here, with the operands, accumulation order and masked epilogue
+    // of bole_factor_gc, written straight into the split planes.  The product
+    // is taken transposed (key rows of tile J as the M operand), so a lane
+    // holds row i = 16I + l16 at the four consecutive columns 16J + 4g .. +3:
+    // the row's scalars are read once and each plane gets one 8-byte store.
+    // Even waves produce the G tiles, odd waves the C tiles: wave w takes the
+    // lower-triangle tiles w/2, w/2 + 4 and w/2 + 8 of its matrix.
+    const bool is_c = w & 1;  // uniform
+#pragma unroll
+    for (int jb = 0; jb < 3; ++jb) {
+      const int tile = (w >> 1) + 4 * jb;
+      if (tile < 10) {
+        const int I = kTileI[tile], J = kTileJ[tile];
+        if (I < nmt) {
+          const int irow = 16 * I + l16, jrow = 16 * J + l16;
+          const int imat = is_c ? 0 : 1;  // Q for C, K for G
+          f32x4 acc = zero_f32x4();
+#pragma unroll
+          for (int kk = 0; kk < SC::KC / 32; ++kk) {
+            if (32 * kk < d_k) {
+              const int io = (imat * kMaxTree + irow) * SC::LROW + 8 * swz<DT>(irow, 4 * kk + g4);
+              const int jo = (kMaxTree + jrow) * SC::LROW + 8 * swz<DT>(jrow, 4 * kk + g4);
+              const bf16x8 xi = *reinterpret_cast<const bf16x8*>(stage + io);
+              const bf16x8 kj = *reinterpret_cast<const bf16x8*>(stage + jo);
+              acc = mfma_bf16(kj, xi, acc);
+              if (DT == BOLE_F32) {
+                const int lo_off = 2 * kMaxTree * SC::LROW;
+                const bf16x8 xil = *reinterpret_cast<const bf16x8*>(stage + lo_off + io);
+                const bf16x8 kjl = *reinterpret_cast<const bf16x8*>(stage + lo_off + jo);
+                acc = mfma_bf16(kjl, xi, acc);
+                acc = mfma_bf16(kj, xil, acc);
+              }
+            }
+          }
+          // branch-free epilogue: every entry is computed and the mask clears
+          // the ones outside it (an overflowing ratio there is cleared too)
+          const int i = irow, j0 = 16 * J + 4 * g4;
+          uint32_t m4 = (uint32_t)(rowApos[i] >> j0) & 15u;
+          const float e2i = rowE2[i];
+          const f32x4 e2j = *reinterpret_cast<const f32x4*>(rowE2 + j0);
+          f32x4 val;
+          if (is_c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = gate_ratio(e2i, e2j[e]) * acc[e];
+              val[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & keep((m4 >> e) & 1u));
+            }
+          } else {
+            const float bi = rowBeta[i];
+            const uint32_t d = (uint32_t)(i - j0);
+            m4 &= ~(d < 4u ? 1u << d : 0u);  // G has no diagonal
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = -(bi * gate_ratio(e2i, e2j[e]) * acc[e]);
+              val[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & keep((m4 >> e) & 1u));
+            }
+          }
+          bf16x4 hi, lo;
+          split_bf16x4(val, hi, lo);
+          const int o = gc_pos(i, j0) + (is_c ? 2 * kGcPlane : 0);
+          *reinterpret_cast<bf16x4*>(gcs + o) = hi;
+          *reinterpret_cast<bf16x4*>(gcs + o + kGcPlane) = lo;
+        }
+      }
+    }
+    __syncthreads();  // -G and C planes complete
+  }
+
+  // ---------------- Diagonal blocks: (I + G_tt)^-1 per 16-row tile --------
+  // In level order G is strictly lower triangular, so each 16x16 diagonal
+  // block N = -G_tt is nilpotent and (I + G_tt)^-1 = sum_m N^m, the finite
+  // Neumann series of Eq. 8 restricted to the tile.  Its index is at most the
+  // number of depths the tile spans (k), and the sum is formed by repeated
+  // squaring, W <- W (I + P), P <- P P, starting from W = I + N: after s rounds
+  // W covers N^0 .. N^(2^(s+1) - 1).  Wave t < 4 owns tile t.  Everything stays
+  // in registers on v_mfma_f32_16x16x16_bf16, whose accumulator layout is its
+  // B operand layout: each product X Y is taken twice, as mfma(X_A, Y_B) (the
+  // B layout of X Y) and as mfma(Y_B, X_A) (the transpose, i.e. the A layout of
+  // X Y), so both operand forms of every factor are at hand.  Operands are
+  // split bf16 hi + lo, three products each, float32 accumulation.
+  if (w < 4 && w < nmt) {
+    const int tb = 16 * w;
+    const int k_span = rowDep[min(tb + 15, T - 1)] - rowDep[tb] + 1;
+    auto id_entry = [&](int e) { return 4 * g4 + e == l16 ? 1.0f : 0.0f; };
+    // N in A layout (row tb + l16, columns tb + 4g .. +3: one 8-byte read) and
+    // in B layout (rows tb + 4g .. +3, column tb + l16)
+    f32x4 Pa, Pb, Wa, Wb;
+    {
+      const int oa = gc_pos(tb + l16, tb + 4 * g4);
+      const bf16x4 ah = *reinterpret_cast<const bf16x4*>(gcs + oa);
+      const bf16x4 al = *reinterpret_cast<const bf16x4*>(gcs + kGcPlane + oa);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ob = gc_pos(tb + 4 * g4 + e, tb + l16);
+        Pa[e] = (float)ah[e] + (float)al[e];
+        Pb[e] = (float)gcs[ob] + (float)gcs[ob + kGcPlane];
+        Wa[e] = Pa[e] + id_entry(e);
+        Wb[e] = Pb[e] + id_entry(e);
+      }
+    }
+    auto mm = [&](const f32x4& xa, const f32x4& yb) {  // A-layout x times B-layout y
+      bf16x4 xh, xl, yh, yl;
+      split_bf16x4(xa, xh, xl);
+      split_bf16x4(yb, yh, yl);
+      f32x4 acc = mfma16_bf16(xh, yh, zero_f32x4());
+      acc = mfma16_bf16(xl, yh, acc);
+      return mfma16_bf16(xh, yl, acc);
+    };
+    for (int span = 2; span < k_span; span *= 2) {
+      const f32x4 Pb2 = mm(Pa, Pb), Pa2 = mm(Pb, Pa);  // P P, both layouts
+      Pa = Pa2;
+      Pb = Pb2;
+      f32x4 Qa, Qb;  // I + P
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Qa[e] = Pa[e] + id_entry(e);
+        Qb[e] = Pb[e] + id_entry(e);
+      }
+      const f32x4 Wb2 = mm(Wa, Qb), Wa2 = mm(Qb, Wa);  // W (I + P), both layouts
+      Wa = Wa2;
+      Wb = Wb2;
+    }
+    bf16x4 wh, wl;
+    split_bf16x4(Wa, wh, wl);
+    invs[w][0][lane] = wh;
+    invs[w][1][lane] = wl;
   }
 
   // ---------------- Phase A: [Q;K] S_pre^(r) ----------------
@@ -172,173 +337,109 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     qs[mt] = zero_f32x4();
     ks[mt] = zero_f32x4();
   }
-  for (int kc0 = 0; kc0 < d_k; kc0 += SC::KC) {
-    if (kc0 > 0) {
+  constexpr bool kOne = FUSED || ONE;
+  for (int kc0 = 0; kc0 < (kOne ? 1 : d_k); kc0 += SC::KC) {
+    if (!kOne && kc0 > 0) {
       __syncthreads();  // every wave is done with the previous chunk
       load_s(kc0);
+      qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, kc0);
+      qk_commit<DT>(stage, qkbuf);
+      __syncthreads();
     }
-    stage_qk<DT>(stage, q, k, rowNode, T, off, H, h, d_k, kc0);
-    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < SC::KC / 32; ++kk) {
       if (kc0 + 32 * kk < d_k) {
         bf16x8 b_hi, b_lo;
         split_bf16x8(sx[kk], b_hi, b_lo);
+        // every row tile runs: staged rows past the tree are zero, and a
+        // per-tile branch would cost a copy of every accumulator at its join
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          if (mt < nmt) {
-            const int row = 16 * mt + l16;
-            const int ro = row * SC::LROW + 8 * swz<DT>(row, 4 * kk + g4);
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(stage + ro);
-            const bf16x8 ak = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::LROW + ro);
-            qs[mt] = mfma_bf16(aq, b_hi, qs[mt]);
-            qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
-            ks[mt] = mfma_bf16(ak, b_hi, ks[mt]);
-            ks[mt] = mfma_bf16(ak, b_lo, ks[mt]);
-            if (DT == BOLE_F32) {
-              const bf16x8 aql =
-                  *reinterpret_cast<const bf16x8*>(stage + 2 * kMaxTree * SC::LROW + ro);
-              const bf16x8 akl =
-                  *reinterpret_cast<const bf16x8*>(stage + 3 * kMaxTree * SC::LROW + ro);
-              qs[mt] = mfma_bf16(aql, b_hi, qs[mt]);
-              ks[mt] = mfma_bf16(akl, b_hi, ks[mt]);
-            }
+          const int row = 16 * mt + l16;
+          const int ro = row * SC::LROW + 8 * swz<DT>(row, 4 * kk + g4);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(stage + ro);
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::LROW + ro);
+          qs[mt] = mfma_bf16(aq, b_hi, qs[mt]);
+          qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
+          ks[mt] = mfma_bf16(ak, b_hi, ks[mt]);
+          ks[mt] = mfma_bf16(ak, b_lo, ks[mt]);
+          if (DT == BOLE_F32) {
+            const bf16x8 aql =
+                *reinterpret_cast<const bf16x8*>(stage + 2 * kMaxTree * SC::LROW + ro);
+            const bf16x8 akl =
+                *reinterpret_cast<const bf16x8*>(stage + 3 * kMaxTree * SC::LROW + ro);
+            qs[mt] = mfma_bf16(aql, b_hi, qs[mt]);
+            ks[mt] = mfma_bf16(akl, b_hi, ks[mt]);
           }
         }
       }
     }
   }
-  if (FUSED) {
-    // d_k fits one staged chunk (checked by the host): each Gram tile is
-    // finished here.  Same operands and accumulation order as bole_factor_gc,
-    // then its masked epilogue, written straight into the split planes.
-#pragma unroll
-    for (int jb = 0; jb < kJobsPerWave; ++jb) {
-      const int job = w + kWaves * jb;
-      if (job < 20) {
-        const int I = kTileI[job >> 1], J = kTileJ[job >> 1];
-        if (I < nmt) {
-          const bool is_c = job & 1;
-          const int arow = 16 * I + l16, brow = 16 * J + l16;
-          const int amat = is_c ? 0 : 1;  // Q for C, K for G
-          f32x4 acc = zero_f32x4();
-#pragma unroll
-          for (int kk = 0; kk < SC::KC / 32; ++kk) {
-            if (32 * kk < d_k) {
-              const int ao = (amat * kMaxTree + arow) * SC::LROW + 8 * swz<DT>(arow, 4 * kk + g4);
-              const int bo = (kMaxTree + brow) * SC::LROW + 8 * swz<DT>(brow, 4 * kk + g4);
-              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(stage + ao);
-              const bf16x8 bh = *reinterpret_cast<const bf16x8*>(stage + bo);
-              acc = mfma_bf16(ah, bh, acc);
-              if (DT == BOLE_F32) {
-                const int lo_off = 2 * kMaxTree * SC::LROW;
-                const bf16x8 al = *reinterpret_cast<const bf16x8*>(stage + lo_off + ao);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(stage + lo_off + bo);
-                acc = mfma_bf16(ah, bl, acc);
-                acc = mfma_bf16(al, bh, acc);
-              }
-            }
-          }
-          const int j = 16 * J + l16;
-          const int nj = rowNode[j];
-          const float lpj = rowLogP[j];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * g4 + e;
-            float val = 0.0f;
-            if (i < T && j < T && ((rowAnc[i] >> nj) & 1ull)) {
-              const float ratio = expf(rowLogP[i] - lpj);
-              if (is_c)
-                val = ratio * acc[e];
-              else if (j != i)
-                val = -(rowBeta[i] * ratio * acc[e]);
-            }
-            const __bf16 hi = (__bf16)val;
-            const int o = gc_pos(i, j) + (is_c ? 2 * kGcPlane : 0);
-            gcs[o] = hi;
-            gcs[o + kGcPlane] = (__bf16)(val - (float)hi);
-          }
-        }
-      }
-    }
-  }
+  __syncthreads();  // diagonal inverses visible
 
   // B0 = D_P QS, R = D_beta (V - D_P KS); rows beyond the tree are exact zeros.
-  // B0 waits in the (now idle) staging area until the readout.
-  f32x4 z[4], u[4];
-  f32x4* b0s = reinterpret_cast<f32x4*>(stage) + w * 4 * 64 + lane;
-  __syncthreads();  // all waves are done reading the staged Q/K; G/C planes complete
-
-  // -G blocks of the Neumann recursion (A fragments, level order)
-  bf16x8 gh[6], gl[6];
-  load_tri_blocks(gcs, gcs + kGcPlane, nmt, lane, gh, gl);
+  f32x4 ru[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    f32x4 b0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int p = 16 * mt + 4 * g4 + e;
       const float P = rowP[p], bt = rowBeta[p];
-      b0[e] = P * qs[mt][e];
-      z[mt][e] = bt * (vv[mt][e] - P * ks[mt][e]);
+      const uint32_t bits = DT == BOLE_BF16 ? (uint32_t)vraw[mt][e] << 16 : (uint32_t)vraw[mt][e];
+      const float vx = __builtin_bit_cast(float, bits & keep(p < T && vin));
+      qs[mt][e] = P * qs[mt][e];
+      ru[mt][e] = bt * (vx - P * ks[mt][e]);
     }
-    b0s[mt * 64] = b0;
-    u[mt] = z[mt];
   }
 
-  // ---------------- Phase C: Neumann recursion (Eq. 8) ----------------
-  // Z <- (-G) Z, U += Z.  -G enters as hi + lo; Z as hi + lo for float32 token
-  // inputs and as one rounded bf16 term for bf16 inputs (U accumulates in fp32).
-  for (int m = 0; m < d_b; ++m) {
-    // rows with depth >= m+1 start at tile I0; Z^(m) is zero before block J0
-    const int I0 = __popcll(ballot64(dep_row < m + 1)) >> 4;
-    const int J0 = __popcll(ballot64(dep_row < m)) >> 5;
-    bf16x8 zh[2], zl[2];
+  // ---------------- Solve (I + G) U = R by 16-row tiles --------------------
+  // U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s).  The sum uses the 32-wide
+  // permuted blocks of -G with the tiles not yet solved entered as zeros; the
+  // lane's own U tiles are the B operand.  Tiles past the tree stay zero.
+  f32x4 u[4];
 #pragma unroll
-    for (int J = 0; J < 2; ++J) {
-      if (DT == BOLE_F32) {
-        split_pair(z[2 * J], z[2 * J + 1], zh[J], zl[J]);
-      } else {
-        zh[J] = to_bf16x8(z[2 * J], z[2 * J + 1]);
-        zl[J] = zero_bf16x8();
-      }
-    }
+  for (int t = 0; t < 4; ++t) u[t] = zero_f32x4();
 #pragma unroll
-    for (int I = 3; I >= 0; --I) {
-      f32x4 acc = zero_f32x4();
-      if (I >= I0 && I < nmt) {
+  for (int t = 0; t < 4; ++t) {
+    if (t < nmt) {
+      f32x4 y = ru[t];
 #pragma unroll
-        for (int J = 0; J <= I / 2; ++J) {
-          if (J >= J0) {
-            const int idx = kBlk(I, J);
-            acc = mfma_bf16(gh[idx], zh[J], acc);
-            acc = mfma_bf16(gl[idx], zh[J], acc);
-            if (DT == BOLE_F32) acc = mfma_bf16(gh[idx], zl[J], acc);
-          }
+      for (int J = 0; J <= t / 2; ++J) {
+        if (2 * J < t) {  // block J holds a solved tile
+          bf16x8 zh, zl;
+          split_pair(u[2 * J], 2 * J + 1 < t ? u[2 * J + 1] : zero_f32x4(), zh, zl);
+          const int o = gc_frag(16 * t + l16, J, g4);
+          const bf16x8 gh = *reinterpret_cast<const bf16x8*>(gcs + o);
+          const bf16x8 gl = *reinterpret_cast<const bf16x8*>(gcs + kGcPlane + o);
+          y = mfma_bf16(gh, zh, y);
+          y = mfma_bf16(gl, zh, y);
+          y = mfma_bf16(gh, zl, y);
         }
       }
-      z[I] = acc;
-      u[I] += acc;
+      bf16x4 yh, yl;
+      split_bf16x4(y, yh, yl);
+      const bf16x4 ih = invs[t][0][lane], il = invs[t][1][lane];
+      f32x4 acc = mfma16_bf16(ih, yh, zero_f32x4());
+      acc = mfma16_bf16(il, yh, acc);
+      u[t] = mfma16_bf16(ih, yl, acc);
     }
   }
 
-  // ---------------- Phase D: readout O = B0 + C U ----------------
-  bf16x8 ch[6], cl[6];
-  load_tri_blocks(gcs + 2 * kGcPlane, gcs + 3 * kGcPlane, nmt, lane, ch, cl);
+  // ---------------- Readout: O = B0 + C U ----------------
   bf16x8 uh[2], ul[2];
 #pragma unroll
   for (int J = 0; J < 2; ++J) split_pair(u[2 * J], u[2 * J + 1], uh[J], ul[J]);
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
-    f32x4 acc = b0s[I * 64];
-    if (I < nmt) {
+    f32x4 acc = qs[I];  // plane rows past tile nmt are zero
 #pragma unroll
-      for (int J = 0; J <= I / 2; ++J) {
-        const int idx = kBlk(I, J);
-        acc = mfma_bf16(ch[idx], uh[J], acc);
-        acc = mfma_bf16(cl[idx], uh[J], acc);
-        acc = mfma_bf16(ch[idx], ul[J], acc);
-      }
+    for (int J = 0; J <= I / 2; ++J) {
+      const int o = gc_frag(16 * I + l16, J, g4);
+      const bf16x8 ch = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
+      const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
+      acc = mfma_bf16(ch, uh[J], acc);
+      acc = mfma_bf16(cl, uh[J], acc);
+      acc = mfma_bf16(ch, ul[J], acc);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -355,6 +456,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 }  // namespace bole
 
 namespace {
+template <int DT, bool FUSED, bool ONE>
+int launch_verify_t(const void* q, const void* k, const void* v, const float* logP,
+                    const float* beta, const float* state_pool, int32_t n_slots,
+                    const int32_t* slot, const float* G, const float* C, const uint64_t* anc,
+                    const int32_t* order, const int32_t* depth, const int32_t* tree_off,
+                    const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                    int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s) {
+  const int NV = (d_v + bole::kBV - 1) / bole::kBV;
+  const dim3 grid(B * H * NV), block(bole::kThreads);
+  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE>), grid, block, 0, s, q, k, v, logP,
+                     beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
+                     tree_depth, B, N, H, d_k, d_v, O, U, err);
+  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
+}
+
 template <bool FUSED>
 int launch_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
                   const float* beta, const float* state_pool, int32_t n_slots,
@@ -362,17 +478,18 @@ int launch_verify(int32_t dtype, const void* q, const void* k, const void* v, co
                   const int32_t* order, const int32_t* depth, const int32_t* tree_off,
                   const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
                   int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s) {
-  const int NV = (d_v + bole::kBV - 1) / bole::kBV;
-  const dim3 grid(B * H * NV), block(bole::kThreads);
-  if (dtype == BOLE_BF16)
-    hipLaunchKernelGGL((bole::verify_kernel<BOLE_BF16, FUSED>), grid, block, 0, s, q, k, v, logP,
-                       beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                       tree_depth, B, N, H, d_k, d_v, O, U, err);
-  else
-    hipLaunchKernelGGL((bole::verify_kernel<BOLE_F32, FUSED>), grid, block, 0, s, q, k, v, logP,
-                       beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                       tree_depth, B, N, H, d_k, d_v, O, U, err);
-  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
+#define BOLE_VERIFY_ARGS                                                                     \
+  q, k, v, logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off, tree_depth, \
+      B, N, H, d_k, d_v, O, U, err, s
+  if (dtype == BOLE_BF16) {
+    if (FUSED || d_k <= bole::StageCfg<BOLE_BF16>::KC)
+      return launch_verify_t<BOLE_BF16, FUSED, true>(BOLE_VERIFY_ARGS);
+    return launch_verify_t<BOLE_BF16, false, false>(BOLE_VERIFY_ARGS);
+  }
+  if (FUSED || d_k <= bole::StageCfg<BOLE_F32>::KC)
+    return launch_verify_t<BOLE_F32, FUSED, true>(BOLE_VERIFY_ARGS);
+  return launch_verify_t<BOLE_F32, false, false>(BOLE_VERIFY_ARGS);
+#undef BOLE_VERIFY_ARGS
 }
 }  // namespace
 

@@ -39,40 +39,51 @@ __device__ __forceinline__ void store_scalar(void* base, int64_t elem, float x) 
 }
 
 // Stage one d_k chunk of the tree's Q and K rows (level order) into LDS as bf16
-// (float32 rows are split into hi and lo planes).  All loads are issued before
-// the first LDS store so one memory round trip covers the whole chunk.
+// (float32 rows are split into hi and lo planes), in two halves: qk_issue puts
+// every global load in flight, qk_commit converts and stores them.  Work issued
+// between the two overlaps the round trip, and loads issued after qk_issue stay
+// in flight while qk_commit waits.
 template <int DT>
-__device__ __forceinline__ void stage_qk(__bf16* stage, const void* q, const void* k,
+struct QkCfg {
+  static constexpr int EPP = DT == BOLE_BF16 ? 8 : 4;   // elements per 16-byte piece
+  static constexpr int PIECES = StageCfg<DT>::KC / EPP;  // pieces per row
+  static constexpr int PER = 2 * kMaxTree * PIECES / kThreads;
+};
+
+template <int DT>
+__device__ __forceinline__ void qk_issue(u16x8* buf, const void* q, const void* k,
                                          const int* rowNode, int T, int off, int H, int h,
                                          int d_k, int kc0) {
-  using SC = StageCfg<DT>;
-  constexpr int EPP = DT == BOLE_BF16 ? 8 : 4;       // elements per 16-byte global piece
-  constexpr int PIECES = SC::KC / EPP;                // pieces per row
-  constexpr int TOTAL = 2 * kMaxTree * PIECES;        // Q and K
-  constexpr int PER = TOTAL / kThreads;
-  u16x8 buf[PER];
+  using QC = QkCfg<DT>;
 #pragma unroll
-  for (int it = 0; it < PER; ++it) {
+  for (int it = 0; it < QC::PER; ++it) {
     const int id = threadIdx.x + kThreads * it;
-    const int mat = id / (kMaxTree * PIECES);
-    const int rem = id - mat * (kMaxTree * PIECES);
-    const int row = rem / PIECES, pc = rem - (rem / PIECES) * PIECES;
-    const int kk = kc0 + EPP * pc;
-    u16x8 val = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (row < T && kk < d_k) {
-      const int64_t e = ((int64_t)(off + rowNode[row]) * H + h) * d_k + kk;
-      val = DT == BOLE_BF16
-                ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat == 0 ? q : k) + e)
-                : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(mat == 0 ? q : k) + e);
-    }
-    buf[it] = val;
+    const int mat = id / (kMaxTree * QC::PIECES);
+    const int rem = id - mat * (kMaxTree * QC::PIECES);
+    const int row = rem / QC::PIECES, pc = rem - (rem / QC::PIECES) * QC::PIECES;
+    const int kk = kc0 + QC::EPP * pc;
+    // unconditional load (row and column clamped into the tree), zeroed after
+    const bool in = row < T && kk < d_k;
+    const int64_t e = ((int64_t)(off + rowNode[min(row, T - 1)]) * H + h) * d_k + (kk < d_k ? kk : 0);
+    const u16x8 val =
+        DT == BOLE_BF16
+            ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat == 0 ? q : k) + e)
+            : *reinterpret_cast<const u16x8*>(reinterpret_cast<const float*>(mat == 0 ? q : k) + e);
+    const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    buf[it] = in ? val : zero;  // a select of a loaded value: the load stays unconditional
   }
+}
+
+template <int DT>
+__device__ __forceinline__ void qk_commit(__bf16* stage, const u16x8* buf) {
+  using SC = StageCfg<DT>;
+  using QC = QkCfg<DT>;
 #pragma unroll
-  for (int it = 0; it < PER; ++it) {
+  for (int it = 0; it < QC::PER; ++it) {
     const int id = threadIdx.x + kThreads * it;
-    const int mat = id / (kMaxTree * PIECES);
-    const int rem = id - mat * (kMaxTree * PIECES);
-    const int row = rem / PIECES, pc = rem - (rem / PIECES) * PIECES;
+    const int mat = id / (kMaxTree * QC::PIECES);
+    const int rem = id - mat * (kMaxTree * QC::PIECES);
+    const int row = rem / QC::PIECES, pc = rem - (rem / QC::PIECES) * QC::PIECES;
     if (DT == BOLE_BF16) {
       *reinterpret_cast<u16x8*>(stage + (mat * kMaxTree + row) * SC::LROW + 8 * swz<DT>(row, pc)) =
           buf[it];
@@ -145,10 +156,9 @@ __device__ __forceinline__ void split_pair(const f32x4& a, const f32x4& b, bf16x
   lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
 }
 
-// Gram tiles (I >= J) computed in the fused variant; job j of a workgroup is
-// tile kTileI/J[j >> 1] of K K^T (j even, for G) or Q K^T (j odd, for C).
+// The ten lower-triangle tiles (I >= J) of a 64x64 Gram product, computed in
+// the fused variant.
 __constant__ constexpr int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ constexpr int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-constexpr int kJobsPerWave = (20 + kWaves - 1) / kWaves;
 
 }  // namespace bole
