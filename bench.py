@@ -27,9 +27,12 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_target_counters.json")
+PROFILES = os.path.join(ROOT, "profiles")
+PROFILE_COUNTERS = os.path.join(PROFILES, "bole_factor_verify_target_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_tree_amd", "csrc", f)
-                  for f in ("verify.hip", "common.h")]
+                  for f in ("verify.hip", "verify_tiles.h", "common.h")]
+# the fused bf16 verify kernel the default step launches (name as rocprofv3 prints it)
+DOMINANT_KERNEL = "verify_kernel<1, true, true>"
 
 
 def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
@@ -54,6 +57,83 @@ def traffic_from_profile(expected_hash):
     if d.get("kernel_source_hash") != expected_hash:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
+    """Turn three rocprofv3 runs of this script (a kernel trace, a FETCH_SIZE
+    pass and a WRITE_SIZE pass, the counter passes preceded by a plain copy of
+    calib_mib MiB) into the text summaries under profiles/ and the counter
+    record the bench line reads its `traffic` from."""
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = ["# Kernel durations, target workload (rocprofv3 --kernel-trace --stats)", "",
+             "Command:", "", "```", commands["trace"], "```", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "bole::" in r["Name"] or "copyBuffer" in r["Name"]:
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} |")
+    with open(os.path.join(PROFILES, "bole_kernels_target_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    def per_dispatch(d, counter):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        dom = [float(r["Counter_Value"]) for r in rows if DOMINANT_KERNEL in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not dom or not copies:
+            raise SystemExit(f"{counter}: dominant kernel or calibration copy missing in {d}")
+        return sum(dom) / len(dom), len(dom), max(copies)
+
+    fetch, n_f, copy_fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, n_w, copy_write = per_dispatch(write_dir, "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+    f_fetch, f_write = calib_kib / copy_fetch, calib_kib / copy_write
+    traffic = (fetch * f_fetch + write * f_write) * 1024.0
+    cfg = W.CONFIGS["target"]
+    algo = np.mean([verify_algorithmic_bytes(W.make_forest(cfg, seed).sizes(), cfg.H, cfg.d_k,
+                                             cfg.d_v, 2) for seed in range(4)])
+    rec = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [n_f, n_w], "copy_mib": calib_mib,
+           "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+           "fetch_scale": f_fetch, "write_scale": f_write,
+           "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": float(algo)}
+    with open(PROFILE_COUNTERS, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    md = ["# HBM traffic of `bole_factor_verify`, target workload (rocprofv3 --pmc)", "",
+          "Commands (one counter per pass; each pass first copies "
+          f"{calib_mib} MiB device-to-device for the calibration):", "", "```",
+          commands["fetch"], commands["write"], "```", "",
+          "| quantity | value |", "|---|---|",
+          f"| FETCH_SIZE per dispatch (KiB) | {fetch:.0f} over {n_f} dispatches |",
+          f"| WRITE_SIZE per dispatch (KiB) | {write:.0f} over {n_w} dispatches |",
+          f"| copy of {calib_mib} MiB: FETCH_SIZE / WRITE_SIZE (KiB) | {copy_fetch:.0f} / "
+          f"{copy_write:.0f} |",
+          f"| scale factors (true / counted) | fetch {f_fetch:.3f}, write {f_write:.3f} |",
+          f"| HBM bytes per launch (scaled) | {traffic / 1e6:.1f} MB |",
+          f"| algorithmic bytes per launch | {algo / 1e6:.1f} MB |",
+          f"| ratio | {traffic / algo:.3f} |", "",
+          f"Kernel source hash: `{rec['kernel_source_hash']}` (verify.hip, verify_tiles.h, "
+          "common.h); bench.py reports `traffic` only while it matches."]
+    with open(os.path.join(PROFILES, "bole_factor_verify_target_counters.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps(rec))
 
 
 def build_states_on_gpu(cfg, B, layer, seed, torch, TreeRound, dev):
@@ -217,7 +297,17 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from three rocprofv3 runs of this script "
+                         "(no GPU needed)")
+    ap.add_argument("--profile-commands", default="",
+                    help="JSON {trace, fetch, write} of the commands that made the runs")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.calibrate_copy_mib or 256,
+                           json.loads(args.profile_commands or "{}") or
+                           {"trace": "?", "fetch": "?", "write": "?"})
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(every (request, head, layer) unit is independent, so a multi-GPU run would "
