@@ -230,7 +230,38 @@ def run_step(s, bole, path="fused"):
         launch(s, bole, which)
 
 
-def time_steps(sets, bole, path, K, torch):
+def capture(torch, fn):
+    """A HIP graph of the launches fn() makes on the current stream (captured on
+    a side stream, as torch requires)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # one uncaptured pass on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(graphs, reps, torch):
+    """Average ms per replay of graphs[i % len(graphs)], i < reps, bracketed by
+    events on the replaying (current) stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_steps_eager(sets, bole, path, K, torch):
+    """The same steps launched one call at a time from Python (bound by the
+    host's launch rate rather than the GPU)."""
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -242,20 +273,26 @@ def time_steps(sets, bole, path, K, torch):
     return t0.elapsed_time(t1) / K
 
 
-def time_kernel(sets, bole, which, reps, torch):
-    """Average duration of one launch of `which`, back to back over the rotated
-    input sets, bracketed by events on the launching (current) stream."""
-    for i in range(len(sets)):
-        launch(sets[i], bole, which)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+def check_graph_replay(s, graph, bole, path, torch):
+    """A captured step must reproduce the eager step exactly: from the same
+    state pool, eager and replayed O, U and committed pool agree bit for bit,
+    on several replays with eager work between them."""
+    pool0 = s.pool.clone()
+    for _ in range(3):
+        s.pool.copy_(pool0)
+        run_step(s, bole, path)
+        ref = (s.O.clone(), s.U.clone(), s.pool.clone())
+        s.pool.copy_(pool0)
+        s.O.zero_()
+        s.U.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (s.O, s.U, s.pool)):
+            if not torch.equal(a, b):
+                raise SystemExit("graph replay differs from the eager step")
+    s.pool.copy_(pool0)
     torch.cuda.synchronize()
-    e0.record()
-    for i in range(reps):
-        launch(sets[i % len(sets)], bole, which)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline(cfg, seed, budget_s=12.0):
@@ -338,13 +375,46 @@ def main():
     for s in sets:
         assert s.rnd.error_bits() == 0, "device error bits set"
 
+    # The step is timed as HIP graph replays (one captured step per input set,
+    # replayed in rotation): launching three kernels per step from Python costs
+    # more host time than the GPU spends on them.
     K = args.steps
-    ms_step = time_steps(sets, bole, args.path, K, torch)
     other = "split" if args.path == "fused" else "fused"
-    ms_other = time_steps(sets, bole, other, max(K // 2, 10), torch)
-    # per-kernel averages: each kernel alone, back to back (same inputs, same stream)
+    R = 4 * len(sets)  # steps per rotation graph
+    singles = [capture(torch, lambda s_=s_: run_step(s_, bole, args.path)) for s_ in sets]
+    check_graph_replay(sets[0], singles[0], bole, args.path, torch)
+
+    def rotation(p):
+        return capture(torch, lambda: [run_step(sets[i % len(sets)], bole, p) for i in range(R)])
+
+    def time_k_steps(p, k, singles_p):
+        """Exactly k steps: k // R rotation replays, then the rest one by one."""
+        rot = rotation(p)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(k // R):
+            rot.replay()
+        for i in range(k % R):
+            singles_p[i % len(sets)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    ms_step = time_k_steps(args.path, K, singles)
+    singles_other = [capture(torch, lambda s_=s_: run_step(s_, bole, other)) for s_ in sets]
+    ms_other = time_k_steps(other, max(K // 2, 10), singles_other)
+    ms_eager = time_steps_eager(sets, bole, args.path, max(K // 2, 10), torch)
+    # per-kernel averages: each kernel alone, 4 x len(sets) launches per graph
+    # over the rotated sets (same inputs, same stream)
     kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "commit")
-    avg = {which: time_kernel(sets, bole, which, max(K, 20), torch) for which in kernels}
+    avg = {}
+    for which in kernels:
+        n_in = 4 * len(sets)
+        g = capture(torch, lambda w_=which: [launch(sets[i % len(sets)], bole, w_)
+                                              for i in range(n_in)])
+        avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     for s_ in sets:
         assert s_.rnd.error_bits() == 0, "device error bits set"
     dominant = "factor_verify" if args.path == "fused" else "verify"
@@ -374,7 +444,9 @@ def main():
                         f"f32 gates and state; step = {' + '.join(STEPS[args.path])}",
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
             "nodes": nodes, "input_sets": len(sets), "path": args.path,
+            "timing": "HIP graph replays: 16 captured steps per graph; kernels: 16 launches per graph",
             "ms_per_step_other_path": {other: ms_other},
+            "ms_per_step_eager_launches": ms_eager,
             "kernel_ms_back_to_back": avg,
         },
         "roofline": {

@@ -446,8 +446,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       const int p = 16 * I + 4 * g4 + e;
       if (I < nmt && p < T && vin) {
         const int64_t at = ((int64_t)(off + rowNode[p]) * H + h) * d_v + vcol;
-        U[at] = u[I][e];
-        store_scalar<DT>(O, at, acc[e]);
+        __builtin_nontemporal_store(u[I][e], U + at);
+        if (DT == BOLE_BF16)
+          __builtin_nontemporal_store(float_to_bf16_bits(acc[e]), reinterpret_cast<uint16_t*>(O) + at);
+        else
+          __builtin_nontemporal_store(acc[e], reinterpret_cast<float*>(O) + at);
       }
     }
   }

@@ -335,3 +335,64 @@ def test_factor_verify_bit_identical_to_two_calls(cases, name):
     eu = block_rel_err(U2.cpu().numpy(), U, f.tree_off)
     say(f"  fused O {eo:.2e}  U {eu:.2e}")
     assert eo <= tolerance(case.cfg) and eu <= tolerance(case.cfg)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture
+
+@pytest.mark.parametrize("name", ["decode", "target"])
+def test_graph_replay_matches_eager(cases, name):
+    """The whole step (prep, fused factor + verify, commit) captured in a HIP
+    graph reproduces the eager launches bit for bit, replay after replay, with
+    eager work and synchronizations between the replays."""
+    from linear_attention_tree_amd import TreeRound, bole
+    from helpers import to_dev
+    case = get_case(cases, name, n_layers=1)
+    f = case.forest
+    say(f"graph replay {name}")
+    d = to_dev(case, 0)
+    rnd = TreeRound(f.parent, f.tree_off, case.cfg.H)
+    t = rnd.topo
+    g = d["g"][None].contiguous()
+    logP = torch.empty_like(g)
+    pool0 = torch.from_numpy(case.S_pre[0]).cuda()
+    pool = pool0.clone()
+    slot = torch.from_numpy(case.slot).cuda()
+    accept = torch.from_numpy(f.accept).cuda()
+    O = torch.empty(f.N, case.cfg.H, case.cfg.d_v, dtype=d["v"].dtype, device="cuda")
+    U = torch.empty(f.N, case.cfg.H, case.cfg.d_v, dtype=torch.float32, device="cuda")
+
+    def step():
+        bole.bole_tree_prep(t.parent, t.tree_off, g, t.depth, t.anc, t.order, t.tree_depth,
+                            logP, rnd.err)
+        bole.bole_factor_verify(d["q"], d["k"], d["v"], logP[0], d["beta"], pool, slot, t.anc,
+                                t.order, t.depth, t.tree_off, t.tree_depth, O, U, rnd.err)
+        bole.bole_commit_path(pool, slot, d["k"], U, logP[0], t.anc, t.tree_off, accept,
+                              rnd.err)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (O.clone(), U.clone(), pool.clone(), logP.clone())
+    assert rnd.error_bits() == 0
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pool.copy_(pool0)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        pool.copy_(pool0)
+        O.zero_()
+        U.zero_()
+        logP.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (O, U, pool, logP)):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (pool0 * 2.0).sum().item()  # eager work between replays
+    assert rnd.error_bits() == 0
