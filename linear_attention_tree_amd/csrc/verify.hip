@@ -117,13 +117,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
   __syncthreads();  // rowNode visible
 
-  // everything below depends on the rows only.  Issue order: row scalars, the
-  // Q/K rows (needed first), then the state slice, which is consumed last.
-  const int64_t tok_l = (int64_t)(off + node_l) * H + h;
-  const int dep_raw = depth[off + node_l];
-  const float lp_raw = logP[tok_l];
-  const float bt_raw = beta[tok_l];
-  const uint64_t an_raw = FUSED ? anc[off + node_l] : 0ull;
+  // everything below depends on the rows only.  Issue order: the Q/K rows
+  // (needed first), the row scalars (wave 0), then the state slice and V,
+  // which are consumed last.
   u16x8 qkbuf[QkCfg<DT>::PER];
   qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, 0);
 
@@ -142,9 +138,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       load_f32x8(Srow + (kidx < d_k ? kidx : 0), sx[kk]);
     }
   };
-  load_s(0);
-  // nothing that waits on a load may be scheduled above this point: every
-  // load of the prologue is in flight before the first wait
+  // nothing that waits on a load may be scheduled above this point: the Q/K
+  // rows are in flight before the first wait
   __builtin_amdgcn_sched_barrier(0);
 
   // park G (negated) and C in LDS, split once into bf16 hi/lo planes
@@ -159,46 +154,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat) * kGcPlane + o) = hi;
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat + 1) * kGcPlane + o) = lo;
   }
-  // depth of level-order row `lane` (nondecreasing in the row index)
-  const bool row_in = lane < T;
-  const int dep_row = row_in ? dep_raw : 0x7fff;
-  // every wave writes the same row tables, and rows past the tree are cleared
-  // by masks, not selects: no branch for the loads to sink into
-  const uint32_t rk = keep(row_in);
-  rowP[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, expf(lp_raw)) & rk);
-  rowBeta[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & rk);
-  rowE2[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, lp_raw * kLog2e) & rk);
-  if (FUSED) {
-    // the row's ancestor mask moved from node ids to level positions, where
-    // four consecutive columns are four consecutive bits
-    uint64_t m = an_raw & (T == 64 ? ~0ull : ((1ull << T) - 1ull)), apos = 0ull;
-    while (m) {
-      apos |= 1ull << posOf[__builtin_ctzll(m)];
-      m &= m - 1ull;
-    }
-    rowApos[lane] = apos & (0ull - (uint64_t)row_in);
-  }
-  rowDep[lane] = dep_row;
-  qk_commit<DT>(stage, qkbuf);  // waits for the Q/K rows (and row scalars) only
-  using VRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
-  VRaw vraw[4][4];
-  {
-    // this lane's V entries (accumulator layout), consumed after phase A and
-    // issued once the Q/K rows are in (so they do not delay them).  Rows past
-    // the tree read row T-1 and a column past d_v reads column 0; the values
-    // are masked when used.
-    const VRaw* vcolp = reinterpret_cast<const VRaw*>(v) + (int64_t)h * d_v + (vin ? vcol : 0);
-    const int64_t vstride = (int64_t)H * d_v;  // elements between node rows
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = min(16 * mt + 4 * g4 + e, T - 1);
-        vraw[mt][e] = vcolp[(int64_t)(off + rowNode[p]) * vstride];
+  if (w == 0) {
+    // The row tables are built by one wave: each row-scalar load touches 64
+    // different cache lines (the rows are H elements apart), so eight copies
+    // would crowd the address units while the Q/K rows stream in.  Rows past
+    // the tree are cleared by masks, not selects (no branch for the loads to
+    // sink into).
+    const int64_t tok_l = (int64_t)(off + node_l) * H + h;
+    const int dep_raw = depth[off + node_l];
+    const float lp_raw = logP[tok_l];
+    const float bt_raw = beta[tok_l];
+    const uint64_t an_raw = FUSED ? anc[off + node_l] : 0ull;
+    const bool row_in = lane < T;
+    const uint32_t rk = keep(row_in);
+    rowP[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, expf(lp_raw)) & rk);
+    rowBeta[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & rk);
+    rowE2[lane] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, lp_raw * kLog2e) & rk);
+    if (FUSED) {
+      // the row's ancestor mask moved from node ids to level positions, where
+      // four consecutive columns are four consecutive bits
+      uint64_t m = an_raw & (T == 64 ? ~0ull : ((1ull << T) - 1ull)), apos = 0ull;
+      while (m) {
+        apos |= 1ull << posOf[__builtin_ctzll(m)];
+        m &= m - 1ull;
       }
+      rowApos[lane] = apos & (0ull - (uint64_t)row_in);
+    }
+    // depth of level-order row `lane` (nondecreasing in the row index)
+    rowDep[lane] = row_in ? dep_raw : 0x7fff;
   }
-  __builtin_amdgcn_sched_barrier(0);
+  qk_commit<DT>(stage, qkbuf);  // waits for the Q/K rows
   __syncthreads();  // staged rows and row tables visible
+  // The state slice and V are requested only once the workgroup's Q/K rows are
+  // in: the memory system serves concurrent requests interleaved, so issued
+  // together (or while sibling waves still wait for their rows) they would
+  // delay the Q/K rows, needed first for the Gram products and the diagonal
+  // blocks, to the end of the whole transfer; issued after them they still
+  // complete as early.
+  load_s(0);
+  __builtin_amdgcn_sched_barrier(0);
 
   if (FUSED) {
     // d_k fits one staged chunk (checked by the host): each Gram tile is
@@ -331,6 +325,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
 
   // ---------------- Phase A: [Q;K] S_pre^(r) ----------------
+  using VRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
+  VRaw vraw[4][4];
+  {
+    // this lane's V entries (accumulator layout), consumed after phase A and requested
+    // only now, after the Gram and diagonal work, so they do not compete with it.  Rows
+    // past the tree read row T-1 and a column past d_v reads column 0; the
+    // values are masked when used.
+    const VRaw* vcolp = reinterpret_cast<const VRaw*>(v) + (int64_t)h * d_v + (vin ? vcol : 0);
+    const int64_t vstride = (int64_t)H * d_v;  // elements between node rows
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = min(16 * mt + 4 * g4 + e, T - 1);
+        vraw[mt][e] = vcolp[(int64_t)(off + rowNode[p]) * vstride];
+      }
+  }
   f32x4 qs[4], ks[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
