@@ -5,17 +5,18 @@
 //
 // One single-wave workgroup per (layer, request, head, 64x64 block of the
 // slot).  Waves are independent: no LDS staging and no barrier.  Each wave
-// derives the path from the ancestor mask and the gate sums held across its
-// lanes, issues its slot loads, then loads its operand fragments straight from
+// issues its slot loads, derives the path from the ancestor mask and the gate
+// sums held across its lanes, then loads its operand fragments straight from
 // global memory (a 16-lane group reads one contiguous row segment per load).
 //
 // The path sum is a [d_k x L_a] x [L_a x d_v] product on
-// v_mfma_f32_16x16x32_bf16 with the path position as K (chunks of 32):
+// v_mfma_f32_16x16x16_bf16 with the path position as K (steps of 16: a path is
+// rarely longer, and each step's fragments are four loads per lane):
 // A = k_j (bf16 exact; float32 keys split hi+lo), B = (P_a/P_j) U_j (float32,
 // split hi+lo).  The accumulator of a 16x16 tile holds four consecutive key
-// columns of one value row, which is one float4 of the slot; it starts as
-// P_a S in float32 and the products accumulate onto it, so every slot element
-// is read once and written once.
+// columns of one value row, which is one float4 of the slot: every slot
+// element is read once and written once, as P_a S + the path product in
+// float32.
 #include <type_traits>
 
 #include "common.h"
@@ -24,7 +25,7 @@ namespace bole {
 
 constexpr int kCommitBlk = 64;    // slot rows / columns per wave
 constexpr int kCommitTiles = 4;   // 16-wide tiles per block side
-constexpr int kPathChunk = 32;    // path positions per MFMA K step
+constexpr int kPathChunk = 16;    // path positions per MFMA K step
 
 template <int DT>
 __global__ __launch_bounds__(64) void commit_kernel(
@@ -68,29 +69,30 @@ __global__ __launch_bounds__(64) void commit_kernel(
   const float* Ul = Umat + layer * u_layer_stride;
   float* S = state_pool + layer * state_layer_stride + ((int64_t)s * H + h) * d_v * d_k;
 
-  // gate sums of every tree node (one per lane) and the accepted node's mask
-  const float lp_lane = lane < T ? lp[(int64_t)(off + lane) * H + h] : 0.0f;
+  // gate sums of every tree node (one per lane; a lane past the tree reads node
+  // T-1, unused) and the accepted node's mask
+  const float lp_lane = lp[(int64_t)(off + min(lane, T - 1)) * H + h];
   const uint64_t tmask = T == 64 ? ~0ull : ((1ull << T) - 1ull);
   const uint64_t path = anc[off + a] & tmask;
 
-  // slot tiles of this block: tile (nt, mt) covers value rows v0 + 16nt .. and
-  // key columns c0 + 16mt ..; the lane's float4 is row 16nt + l16, columns
-  // 16mt + 4g4 .. +3
+  // The slot tiles go out next, before the chain is waited on (issued after
+  // the chain, the commit was measured to finish later).  A tile past
+  // d_k or d_v (partial block) reads tile (0, 0) instead and is never stored, so
+  // every load is unconditional and in bounds.
   const int c0 = kCommitBlk * bc, v0 = kCommitBlk * bv;
-  f32x4 acc[kCommitTiles][kCommitTiles];
+  f32x4 prod[kCommitTiles][kCommitTiles], sv[kCommitTiles][kCommitTiles];
   bool tok[kCommitTiles][kCommitTiles];
 #pragma unroll
   for (int nt = 0; nt < kCommitTiles; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < kCommitTiles; ++mt) {
-      // a tile past d_k or d_v (partial block) reads tile (0, 0) instead and is
-      // never stored, so every load is unconditional and in bounds
+      prod[nt][mt] = zero_f32x4();
       tok[nt][mt] = c0 + 16 * mt < d_k && v0 + 16 * nt < d_v;
       const int tv = tok[nt][mt] ? 16 * nt : 0, tc = tok[nt][mt] ? 16 * mt : 0;
-      acc[nt][mt] =
-          *reinterpret_cast<const f32x4*>(S + (v0 + tv + l16) * d_k + c0 + tc + 4 * g4);
+      sv[nt][mt] = *reinterpret_cast<const f32x4*>(S + (v0 + tv + l16) * d_k + c0 + tc + 4 * g4);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   const float lpa = __shfl(lp_lane, a);
   const float Pa = expf(lpa);
@@ -102,91 +104,85 @@ __global__ __launch_bounds__(64) void commit_kernel(
   }
   __syncthreads();  // a single wave: orders the LDS writes before the reads
 
+  // Tile (nt, mt) of this block covers value rows v0 + 16nt .. and key columns
+  // c0 + 16mt ..; the lane's float4 is row 16nt + l16, columns 16mt + 4g4 .. +3.
+  // The path products accumulate from zero; P_a S is added at the end.
   const int64_t hk = (int64_t)h * d_k, hv = (int64_t)h * d_v;
-  // at least one pass, which applies P_a (an empty path adds nothing)
-  for (int kc = 0; kc == 0 || kc < La; kc += kPathChunk) {
-    // the lane's 8 path positions of this chunk
-    int64_t rk[8], rv[8];
-    float wt[8];
-    bool live[8];
+  for (int kc = 0; kc < La; kc += kPathChunk) {
+    // the lane's 4 path positions of this step
+    int64_t rk[4], rv[4];
+    float wt[4];
+    bool live[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int p = kc + 8 * g4 + e;
+    for (int e = 0; e < 4; ++e) {
+      const int p = kc + 4 * g4 + e;
       live[e] = p < La;
       const int node = live[e] ? pj[p] : 0;
       wt[e] = live[e] ? wj[p] : 0.0f;
       rk[e] = (int64_t)(off + node) * H * d_k + hk;
       rv[e] = (int64_t)(off + node) * H * d_v + hv;
     }
-    // Every fragment load of the chunk is issued before any value is used.
+    // Every fragment load of the step is issued before any value is used.
     // Loads are unconditional (a dead position reads node 0, a column past d_k
     // reads c0, a row past d_v reads v0) and masked afterwards.
     using KRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
-    KRaw kraw[kCommitTiles][8];
-    float uraw[kCommitTiles][8];
+    KRaw kraw[kCommitTiles][4];
+    float uraw[kCommitTiles][4];
     const KRaw* kl = reinterpret_cast<const KRaw*>(kmat) + layer * k_layer_stride;
 #pragma unroll
     for (int mt = 0; mt < kCommitTiles; ++mt) {
       const int c = c0 + 16 * mt + l16;
       const int cc = c < d_k ? c : c0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kraw[mt][e] = kl[rk[e] + cc];
+      for (int e = 0; e < 4; ++e) kraw[mt][e] = kl[rk[e] + cc];
     }
 #pragma unroll
     for (int nt = 0; nt < kCommitTiles; ++nt) {
       const int v = v0 + 16 * nt + l16;
       const int vv = v < d_v ? v : v0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) uraw[nt][e] = Ul[rv[e] + vv];
+      for (int e = 0; e < 4; ++e) uraw[nt][e] = Ul[rv[e] + vv];
     }
     __builtin_amdgcn_sched_barrier(0);
     // A fragments: k_j[c] for c = c0 + 16mt + l16 (bf16 keys are exact)
-    bf16x8 ah[kCommitTiles], al[kCommitTiles];
+    bf16x4 ah[kCommitTiles], al[kCommitTiles];
 #pragma unroll
     for (int mt = 0; mt < kCommitTiles; ++mt) {
       const bool cok = c0 + 16 * mt + l16 < d_k;
       if (DT == BOLE_BF16) {
-        u16x8 raw;
+        u16x4 raw;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = kraw[mt][e] & (uint16_t)keep(live[e] && cok);
-        ah[mt] = __builtin_bit_cast(bf16x8, raw);
-        al[mt] = zero_bf16x8();
+        for (int e = 0; e < 4; ++e) raw[e] = kraw[mt][e] & (uint16_t)keep(live[e] && cok);
+        ah[mt] = __builtin_bit_cast(bf16x4, raw);
+        al[mt] = bf16x4{};
       } else {
-        float x[8];
+        f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 4; ++e)
           x[e] = __builtin_bit_cast(float, (uint32_t)kraw[mt][e] & keep(live[e] && cok));
-        split_bf16x8(x, ah[mt], al[mt]);
+        split_bf16x4(x, ah[mt], al[mt]);
       }
     }
     // B fragments: (P_a/P_j) U_j[v] for v = v0 + 16nt + l16, split hi+lo
-    bf16x8 bh[kCommitTiles], bl[kCommitTiles];
+    bf16x4 bh[kCommitTiles], bl[kCommitTiles];
 #pragma unroll
     for (int nt = 0; nt < kCommitTiles; ++nt) {
       const bool vok = v0 + 16 * nt + l16 < d_v;
-      float x[8];
+      f32x4 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 4; ++e)
         x[e] = __builtin_bit_cast(
             float, __builtin_bit_cast(uint32_t, wt[e] * uraw[nt][e]) & keep(live[e] && vok));
-      split_bf16x8(x, bh[nt], bl[nt]);
-    }
-    // the slot tiles are waited on only now, after the fragment loads are issued
-    if (kc == 0) {
-#pragma unroll
-      for (int nt = 0; nt < kCommitTiles; ++nt) {
-#pragma unroll
-        for (int mt = 0; mt < kCommitTiles; ++mt) acc[nt][mt] = Pa * acc[nt][mt];
-      }
+      split_bf16x4(x, bh[nt], bl[nt]);
     }
     // D[c][v] += sum_p A[c][p] B[p][v]
 #pragma unroll
     for (int nt = 0; nt < kCommitTiles; ++nt) {
 #pragma unroll
       for (int mt = 0; mt < kCommitTiles; ++mt) {
-        acc[nt][mt] = mfma_bf16(ah[mt], bh[nt], acc[nt][mt]);
-        acc[nt][mt] = mfma_bf16(ah[mt], bl[nt], acc[nt][mt]);
-        if (DT == BOLE_F32) acc[nt][mt] = mfma_bf16(al[mt], bh[nt], acc[nt][mt]);
+        prod[nt][mt] = mfma16_bf16(ah[mt], bh[nt], prod[nt][mt]);
+        prod[nt][mt] = mfma16_bf16(ah[mt], bl[nt], prod[nt][mt]);
+        if (DT == BOLE_F32) prod[nt][mt] = mfma16_bf16(al[mt], bh[nt], prod[nt][mt]);
       }
     }
   }
@@ -194,9 +190,12 @@ __global__ __launch_bounds__(64) void commit_kernel(
   for (int nt = 0; nt < kCommitTiles; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < kCommitTiles; ++mt) {
-      if (tok[nt][mt])
-        *reinterpret_cast<f32x4*>(S + (v0 + 16 * nt + l16) * d_k + c0 + 16 * mt + 4 * g4) =
-            acc[nt][mt];
+      if (tok[nt][mt]) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = Pa * sv[nt][mt][e] + prod[nt][mt][e];
+        *reinterpret_cast<f32x4*>(S + (v0 + 16 * nt + l16) * d_k + c0 + 16 * mt + 4 * g4) = o;
+      }
     }
   }
 }
