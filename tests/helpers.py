@@ -50,9 +50,10 @@ def prefix_slots(cfg: W.Config, layer: int, n_slots: int, slot: np.ndarray, seed
     return S
 
 
-def make_case(name: str, seed: int = 0, n_layers: Optional[int] = None, forest=None,
+def make_case(name, seed: int = 0, n_layers: Optional[int] = None, forest=None,
               prefix_units=None, extra_slots: int = 3) -> Case:
-    cfg = W.CONFIGS[name]
+    """`name` is a workload name or a Config."""
+    cfg = W.CONFIGS[name] if isinstance(name, str) else name
     forest = forest if forest is not None else W.make_forest(cfg, seed)
     L = cfg.L if n_layers is None else n_layers
     layers = [W.make_layer(cfg, forest.N, l, seed) for l in range(L)]
@@ -120,7 +121,7 @@ def to_dev(case: Case, l: int, device="cuda"):
                 dtype=tdt)
 
 
-def gpu_round(case: Case, layers=None, commit=True, device="cuda"):
+def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False):
     """Run prep, factor, verify (and commit) on the GPU through the C ABI.
 
     Returns dict with per-layer O, U (numpy float64), the state pools after
@@ -137,7 +138,8 @@ def gpu_round(case: Case, layers=None, commit=True, device="cuda"):
     pools = torch.stack([torch.from_numpy(case.S_pre[l]) for l in layers]).to(device)
     Os, Us = [], []
     for li, d in enumerate(dev):
-        O, U = rnd.layer(d["q"], d["k"], d["v"], logP[li], d["beta"], pools[li], slot)
+        O, U = rnd.layer(d["q"], d["k"], d["v"], logP[li], d["beta"], pools[li], slot,
+                         fused=fused)
         Os.append(O)
         Us.append(U)
     out = dict(logP=logP.cpu().numpy(), depth=rnd.topo.depth.cpu().numpy(),
