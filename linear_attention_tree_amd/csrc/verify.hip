@@ -201,63 +201,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     // is taken transposed (key rows of tile J as the M operand), so a lane
     // holds row i = 16I + l16 at the four consecutive columns 16J + 4g .. +3:
     // the row's scalars are read once and each plane gets one 8-byte store.
-    // Even waves produce the G tiles, odd waves the C tiles: wave w takes the
-    // lower-triangle tiles w/2, w/2 + 4 and w/2 + 8 of its matrix.
-    const bool is_c = w & 1;  // uniform
+    // Wave w takes lower-triangle tile w (and waves 0, 1 tiles 8, 9) of both
+    // products: the K rows of tile J, the mask and the gate ratios are shared
+    // by the G and C entries of a tile.
 #pragma unroll
-    for (int jb = 0; jb < 3; ++jb) {
-      const int tile = (w >> 1) + 4 * jb;
+    for (int jb = 0; jb < 2; ++jb) {
+      const int tile = w + kWaves * jb;
       if (tile < 10) {
         const int I = kTileI[tile], J = kTileJ[tile];
         if (I < nmt) {
           const int irow = 16 * I + l16, jrow = 16 * J + l16;
-          const int imat = is_c ? 0 : 1;  // Q for C, K for G
-          f32x4 acc = zero_f32x4();
+          f32x4 accC = zero_f32x4(), accG = zero_f32x4();
 #pragma unroll
           for (int kk = 0; kk < SC::KC / 32; ++kk) {
             if (32 * kk < d_k) {
-              const int io = (imat * kMaxTree + irow) * SC::LROW + 8 * swz<DT>(irow, 4 * kk + g4);
+              const int io = irow * SC::LROW + 8 * swz<DT>(irow, 4 * kk + g4);
               const int jo = (kMaxTree + jrow) * SC::LROW + 8 * swz<DT>(jrow, 4 * kk + g4);
-              const bf16x8 xi = *reinterpret_cast<const bf16x8*>(stage + io);
+              const bf16x8 qi = *reinterpret_cast<const bf16x8*>(stage + io);
+              const bf16x8 ki = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::LROW + io);
               const bf16x8 kj = *reinterpret_cast<const bf16x8*>(stage + jo);
-              acc = mfma_bf16(kj, xi, acc);
+              accC = mfma_bf16(kj, qi, accC);
+              accG = mfma_bf16(kj, ki, accG);
               if (DT == BOLE_F32) {
                 const int lo_off = 2 * kMaxTree * SC::LROW;
-                const bf16x8 xil = *reinterpret_cast<const bf16x8*>(stage + lo_off + io);
+                const bf16x8 qil = *reinterpret_cast<const bf16x8*>(stage + lo_off + io);
+                const bf16x8 kil =
+                    *reinterpret_cast<const bf16x8*>(stage + lo_off + kMaxTree * SC::LROW + io);
                 const bf16x8 kjl = *reinterpret_cast<const bf16x8*>(stage + lo_off + jo);
-                acc = mfma_bf16(kjl, xi, acc);
-                acc = mfma_bf16(kj, xil, acc);
+                accC = mfma_bf16(kjl, qi, accC);
+                accC = mfma_bf16(kj, qil, accC);
+                accG = mfma_bf16(kjl, ki, accG);
+                accG = mfma_bf16(kj, kil, accG);
               }
             }
           }
           // branch-free epilogue: every entry is computed and the mask clears
           // the ones outside it (an overflowing ratio there is cleared too)
           const int i = irow, j0 = 16 * J + 4 * g4;
-          uint32_t m4 = (uint32_t)(rowApos[i] >> j0) & 15u;
-          const float e2i = rowE2[i];
+          const uint32_t m4 = (uint32_t)(rowApos[i] >> j0) & 15u;
+          const uint32_t d = (uint32_t)(i - j0);
+          const uint32_t m4g = m4 & ~(d < 4u ? 1u << d : 0u);  // G has no diagonal
+          const float e2i = rowE2[i], bi = rowBeta[i];
           const f32x4 e2j = *reinterpret_cast<const f32x4*>(rowE2 + j0);
-          f32x4 val;
-          if (is_c) {
+          f32x4 vc, vg;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = gate_ratio(e2i, e2j[e]) * acc[e];
-              val[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & keep((m4 >> e) & 1u));
-            }
-          } else {
-            const float bi = rowBeta[i];
-            const uint32_t d = (uint32_t)(i - j0);
-            m4 &= ~(d < 4u ? 1u << d : 0u);  // G has no diagonal
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = -(bi * gate_ratio(e2i, e2j[e]) * acc[e]);
-              val[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & keep((m4 >> e) & 1u));
-            }
+          for (int e = 0; e < 4; ++e) {
+            const float ratio = gate_ratio(e2i, e2j[e]);
+            const float c = ratio * accC[e];
+            const float gneg = -(bi * ratio * accG[e]);
+            vc[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c) & keep((m4 >> e) & 1u));
+            vg[e] =
+                __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gneg) & keep((m4g >> e) & 1u));
           }
           bf16x4 hi, lo;
-          split_bf16x4(val, hi, lo);
-          const int o = gc_pos(i, j0) + (is_c ? 2 * kGcPlane : 0);
+          const int o = gc_pos(i, j0);
+          split_bf16x4(vg, hi, lo);
           *reinterpret_cast<bf16x4*>(gcs + o) = hi;
           *reinterpret_cast<bf16x4*>(gcs + o + kGcPlane) = lo;
+          split_bf16x4(vc, hi, lo);
+          *reinterpret_cast<bf16x4*>(gcs + o + 2 * kGcPlane) = hi;
+          *reinterpret_cast<bf16x4*>(gcs + o + 3 * kGcPlane) = lo;
         }
       }
     }
