@@ -24,9 +24,10 @@
 //  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
 //           a permuted K order (load_tri_blocks) that makes the lane's own U
 //           tiles the B operand: U never leaves registers.
-//  Readout  O = B0 + C U; O (token dtype) and the compact float32 U are written
-//           back to the nodes' rows.  Every operand is split hi + lo, float32
-//           accumulation.
+//  Readout  O = B0 + C U.  Every operand is split hi + lo, float32 accumulation.
+//  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
+//           leave as 4-element pieces of the nodes' rows; V arrives the same
+//           way, as 16-byte row pieces staged for the accumulator layout.
 #include <type_traits>
 
 #include "verify_tiles.h"
@@ -47,7 +48,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int32_t* __restrict__ order,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ tree_off,
     const int32_t* __restrict__ tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
-    int32_t d_v, void* __restrict__ O, float* __restrict__ U, uint32_t* __restrict__ err) {
+    int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf,
+    uint32_t* __restrict__ err) {
   using SC = StageCfg<DT>;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::LROW];
   // planes: -G hi, -G lo, C hi, C lo
@@ -328,22 +330,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
 
   // ---------------- Phase A: [Q;K] S_pre^(r) ----------------
-  using VRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
-  VRaw vraw[4][4];
+  // V rows of the workgroup's value columns, requested only now (after the
+  // Gram and diagonal work, so they do not compete with it) as 16-byte row
+  // pieces, held in registers through phase A and staged through LDS for the
+  // accumulator layout afterwards.  Rows past the tree read row T-1 and pieces
+  // past d_v column 0; both are zeroed.  Without kVecV every piece reads the
+  // aligned block holding v[0] and V is fetched element-wise after phase A.
+  using VC = VTileCfg<DT>;
+  using VElem = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
+  const bool vvec = vecf & kVecV;
+  u16x8 vpc[VC::PER];
   {
-    // this lane's V entries (accumulator layout), consumed after phase A and requested
-    // only now, after the Gram and diagonal work, so they do not compete with it.  Rows
-    // past the tree read row T-1 and a column past d_v reads column 0; the
-    // values are masked when used.
-    const VRaw* vcolp = reinterpret_cast<const VRaw*>(v) + (int64_t)h * d_v + (vin ? vcol : 0);
-    const int64_t vstride = (int64_t)H * d_v;  // elements between node rows
+    const u16x8* vsafe = reinterpret_cast<const u16x8*>(reinterpret_cast<uintptr_t>(v) & ~uintptr_t(15));
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = min(16 * mt + 4 * g4 + e, T - 1);
-        vraw[mt][e] = vcolp[(int64_t)(off + rowNode[p]) * vstride];
-      }
+    for (int it = 0; it < VC::PER; ++it) {
+      const int id = threadIdx.x + kThreads * it;
+      const int row = id / VC::PPR, col = kBV * r + VC::EPP * (id % VC::PPR);
+      const bool in = row < T && col < d_v;
+      const int64_t e =
+          ((int64_t)(off + rowNode[min(row, T - 1)]) * H + h) * d_v + (col < d_v ? col : 0);
+      const u16x8* src = vvec ? reinterpret_cast<const u16x8*>(reinterpret_cast<const VElem*>(v) + e)
+                              : vsafe;
+      const u16x8 val = *src;
+      vpc[it] = in ? val : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
   f32x4 qs[4], ks[4];
 #pragma unroll
@@ -389,7 +399,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       }
     }
   }
-  __syncthreads();  // diagonal inverses visible
+  __syncthreads();  // diagonal inverses visible; staged Q/K rows no longer read
+
+  // V tile into LDS (over the staged rows)
+  VElem* vt = reinterpret_cast<VElem*>(stage);
+  if (vvec) {
+#pragma unroll
+    for (int it = 0; it < VC::PER; ++it) {
+      const int id = threadIdx.x + kThreads * it;
+      const int row = id / VC::PPR, c = VC::EPP * (id % VC::PPR);
+      *reinterpret_cast<u16x8*>(vt + vtile_idx(row, c)) = vpc[it];
+    }
+  } else {
+    for (int it = 0; it < kMaxTree * kBV / kThreads; ++it) {
+      const int id = threadIdx.x + kThreads * it;
+      const int row = id / kBV, c = id % kBV, col = kBV * r + c;
+      VElem x = 0;
+      if (row < T && col < d_v)
+        x = reinterpret_cast<const VElem*>(v)[((int64_t)(off + rowNode[row]) * H + h) * d_v + col];
+      vt[vtile_idx(row, c)] = x;
+    }
+  }
+  __syncthreads();  // V tile visible
 
   // B0 = D_P QS, R = D_beta (V - D_P KS); rows beyond the tree are exact zeros.
   f32x4 ru[4];
@@ -399,8 +430,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int e = 0; e < 4; ++e) {
       const int p = 16 * mt + 4 * g4 + e;
       const float P = rowP[p], bt = rowBeta[p];
-      const uint32_t bits = DT == BOLE_BF16 ? (uint32_t)vraw[mt][e] << 16 : (uint32_t)vraw[mt][e];
-      const float vx = __builtin_bit_cast(float, bits & keep(p < T && vin));
+      const VElem raw = vt[vtile_idx(p, vloc)];
+      const float vx = __builtin_bit_cast(float, DT == BOLE_BF16 ? (uint32_t)raw << 16 : (uint32_t)raw);
       qs[mt][e] = P * qs[mt][e];
       ru[mt][e] = bt * (vx - P * ks[mt][e]);
     }
@@ -455,16 +486,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       acc = mfma_bf16(cl, uh[J], acc);
       acc = mfma_bf16(ch, ul[J], acc);
     }
+    qs[I] = acc;
+  }
+
+  // ---------------- Store U and O through LDS ----------------
+  // The tiles are written to LDS in the accumulator layout and leave as 4-element
+  // pieces of the nodes' rows (16 bytes of U, 8 or 16 of O per lane).
+  using OElem = std::conditional_t<DT == BOLE_BF16, uint16_t, float>;
+  __syncthreads();  // every wave is done with the V tile and the C planes
+  float* ut = reinterpret_cast<float*>(stage);
+  OElem* ot = reinterpret_cast<OElem*>(gcs);
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = 16 * I + 4 * g4 + e;
-      if (I < nmt && p < T && vin) {
-        const int64_t at = ((int64_t)(off + rowNode[p]) * H + h) * d_v + vcol;
-        __builtin_nontemporal_store(u[I][e], U + at);
+      const int idx = vtile_idx(16 * I + 4 * g4 + e, vloc);
+      ut[idx] = u[I][e];
+      if (DT == BOLE_BF16)
+        ot[idx] = float_to_bf16_bits(qs[I][e]);
+      else
+        ot[idx] = qs[I][e];
+    }
+  }
+  __syncthreads();  // output tiles visible
+  if (vecf & kVecOut) {
+#pragma unroll
+    for (int it = 0; it < kMaxTree * kBV / 4 / kThreads; ++it) {
+      const int id = threadIdx.x + kThreads * it;
+      const int row = id / (kBV / 4), c = 4 * (id % (kBV / 4)), col = kBV * r + c;
+      if (row < T && col < d_v) {
+        const int64_t at = ((int64_t)(off + rowNode[row]) * H + h) * d_v + col;
+        const int idx = vtile_idx(row, c);
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ut + idx),
+                                    reinterpret_cast<f32x4*>(U + at));
         if (DT == BOLE_BF16)
-          __builtin_nontemporal_store(float_to_bf16_bits(acc[e]), reinterpret_cast<uint16_t*>(O) + at);
+          __builtin_nontemporal_store(*reinterpret_cast<const u16x4*>(ot + idx),
+                                      reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(O) + at));
         else
-          __builtin_nontemporal_store(acc[e], reinterpret_cast<float*>(O) + at);
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ot + idx),
+                                      reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + at));
+      }
+    }
+  } else {
+    for (int it = 0; it < kMaxTree * kBV / kThreads; ++it) {
+      const int id = threadIdx.x + kThreads * it;
+      const int row = id / kBV, c = id % kBV, col = kBV * r + c;
+      if (row < T && col < d_v) {
+        const int64_t at = ((int64_t)(off + rowNode[row]) * H + h) * d_v + col;
+        const int idx = vtile_idx(row, c);
+        U[at] = ut[idx];
+        reinterpret_cast<OElem*>(O)[at] = ot[idx];
       }
     }
   }
@@ -482,9 +553,13 @@ int launch_verify_t(const void* q, const void* k, const void* v, const float* lo
                     int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s) {
   const int NV = (d_v + bole::kBV - 1) / bole::kBV;
   const dim3 grid(B * H * NV), block(bole::kThreads);
+  const int esize = DT == BOLE_BF16 ? 2 : 4;
+  const bool v_ok = d_v % (16 / esize) == 0 && (uintptr_t)v % 16 == 0;
+  const bool out_ok = d_v % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)O % (4 * esize) == 0;
+  const int vecf = (v_ok ? bole::kVecV : 0) | (out_ok ? bole::kVecOut : 0);
   hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE>), grid, block, 0, s, q, k, v, logP,
                      beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                     tree_depth, B, N, H, d_k, d_v, O, U, err);
+                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, err);
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 

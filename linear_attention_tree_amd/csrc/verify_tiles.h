@@ -38,6 +38,29 @@ __device__ __forceinline__ void store_scalar(void* base, int64_t elem, float x) 
     reinterpret_cast<float*>(base)[elem] = x;
 }
 
+// A [64 rows x kBV columns] tile of the workgroup's value columns in LDS (V on
+// the way in, U and O on the way out), row-major with the columns XOR-swizzled
+// in blocks of 16 by (row / 4) % 4.  Accumulator-layout accesses (a wave's 16
+// columns at rows 4g + e, g = 0..3) then hit four different bank groups, and
+// the 4- and 8-element row pieces moved to and from global memory stay
+// contiguous.
+__device__ __forceinline__ int vtile_idx(int row, int col) {
+  return row * kBV + (col ^ (((row >> 2) & 3) << 4));
+}
+
+// Bit flags of the value-tile transfers, set by the host.
+// kVecV: d_v is a multiple of the elements in 16 bytes of v and v is 16-byte
+// aligned, so V rows move as 16-byte pieces.  kVecOut: d_v % 4 == 0 and U and O
+// are aligned for 4-element pieces.
+constexpr int kVecV = 1, kVecOut = 2;
+
+template <int DT>
+struct VTileCfg {
+  static constexpr int EPP = DT == BOLE_BF16 ? 8 : 4;    // elements per 16-byte piece
+  static constexpr int PPR = kBV / EPP;                   // pieces per tile row
+  static constexpr int PER = kMaxTree * PPR / kThreads;   // pieces per thread
+};
+
 // Stage one d_k chunk of the tree's Q and K rows (level order) into LDS as bf16
 // (float32 rows are split into hi and lo planes), in two halves: qk_issue puts
 // every global load in flight, qk_commit converts and stores them.  Work issued

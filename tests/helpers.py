@@ -121,11 +121,22 @@ def to_dev(case: Case, l: int, device="cuda"):
                 dtype=tdt)
 
 
-def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False):
+def offset_copy(t, dtype=None):
+    """t's values in a contiguous buffer that starts one element past the
+    allocation, so it is not 16-byte aligned."""
+    import torch
+    flat = torch.zeros(t.numel() + 1, dtype=dtype or t.dtype, device=t.device)
+    view = flat[1:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, misalign=False):
     """Run prep, factor, verify (and commit) on the GPU through the C ABI.
 
-    Returns dict with per-layer O, U (numpy float64), the state pools after
-    commit, the prep outputs and the error word."""
+    misalign: v, O and U live one element past an aligned address (the kernels'
+    element-wise fallbacks).  Returns dict with per-layer O, U (numpy float64),
+    the state pools after commit, the prep outputs and the error word."""
     import torch
     from linear_attention_tree_amd import TreeRound
     f = case.forest
@@ -138,7 +149,12 @@ def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False):
     pools = torch.stack([torch.from_numpy(case.S_pre[l]) for l in layers]).to(device)
     Os, Us = [], []
     for li, d in enumerate(dev):
-        O, U = rnd.layer(d["q"], d["k"], d["v"], logP[li], d["beta"], pools[li], slot,
+        v, O, U = d["v"], None, None
+        if misalign:
+            v = offset_copy(v)
+            O = offset_copy(torch.empty_like(v))
+            U = offset_copy(torch.empty(v.shape, dtype=torch.float32, device=v.device))
+        O, U = rnd.layer(d["q"], d["k"], v, logP[li], d["beta"], pools[li], slot, O=O, U=U,
                          fused=fused)
         Os.append(O)
         Us.append(U)

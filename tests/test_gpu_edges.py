@@ -47,9 +47,9 @@ def fused_ok(cfg):
     return cfg.d_k <= (128 if cfg.dtype == "bf16" else 64)
 
 
-def check(case, fused, label):
+def check(case, fused, label, misalign=False):
     tol = tolerance(case.cfg)
-    out = gpu_round(case, fused=fused)
+    out = gpu_round(case, fused=fused, misalign=misalign)
     assert out["err"] == 0
     O, U, S_new = oracle_layer(case, 0)
     f = case.forest
@@ -120,3 +120,14 @@ def test_gate_products_underflow():
     say("gate products underflow")
     check(case, False, "split")
     check(case, True, "split")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_token_buffers(dtype):
+    """v, O and U one element past an aligned address: V and the outputs move
+    element by element instead of in 16-byte row pieces."""
+    cfg = edge_cfg(f"unaligned_{dtype}", 45, dtype, 64, 48)
+    case = make_case(cfg, forest=mixed_forest(4), n_layers=1)
+    say(f"unaligned token buffers {dtype}")
+    check(case, False, "split", misalign=True)
+    check(case, True, "split", misalign=True)
