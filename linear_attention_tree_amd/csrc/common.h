@@ -43,6 +43,17 @@ __device__ __forceinline__ void split_bf16x4(const f32x4& x, bf16x4& hi, bf16x4&
   lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), bf16x4);
 }
 
+// Vector stores at device scope (sc1): the line is written through the L2 at
+// once rather than left dirty in it.  A kernel ends only once its dirty L2
+// lines are written back, so output written late in a kernel would otherwise
+// be written back after the last wave has finished.
+__device__ __forceinline__ void store_sc1(float* p, const f32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_sc1(uint16_t* p, const u16x4& v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ f32x4 zero_f32x4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
