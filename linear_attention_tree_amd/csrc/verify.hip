@@ -133,9 +133,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   float sx[SC::KC / 32][8];
   // K positions past d_k read the row's first entries instead: they meet staged
   // Q/K columns that are zero.  Lanes past d_v compute columns never stored.
-  auto load_s = [&](int kc0) {
+  auto load_s = [&](int kc0, int k0, int k1) {
 #pragma unroll
-    for (int kk = 0; kk < SC::KC / 32; ++kk) {
+    for (int kk = k0; kk < k1; ++kk) {
       const int kidx = kc0 + 32 * kk + 8 * g4;
       load_f32x8(Srow + (kidx < d_k ? kidx : 0), sx[kk]);
     }
@@ -192,8 +192,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // together (or while sibling waves still wait for their rows) they would
   // delay the Q/K rows, needed first for the Gram products and the diagonal
   // blocks, to the end of the whole transfer; issued after them they still
-  // complete as early.
-  load_s(0);
+  // complete as early.  Issuing the slice stalls each wave while the address
+  // unit works through it, so the fused variant issues half of it before its
+  // first Gram tile and half after, where the stall overlaps Gram work.
+  constexpr int kSChunks = SC::KC / 32, kSHalf = SC::KC / 64;
+  load_s(0, 0, FUSED ? kSHalf : kSChunks);
   __builtin_amdgcn_sched_barrier(0);
 
   if (FUSED) {
@@ -203,12 +206,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     // is taken transposed (key rows of tile J as the M operand), so a lane
     // holds row i = 16I + l16 at the four consecutive columns 16J + 4g .. +3:
     // the row's scalars are read once and each plane gets one 8-byte store.
-    // Wave w takes lower-triangle tile w (and waves 0, 1 tiles 8, 9) of both
+    // Wave w takes lower-triangle tile w (and waves 4, 5 tiles 8, 9) of both
     // products: the K rows of tile J, the mask and the gate ratios are shared
-    // by the G and C entries of a tile.
+    // by the G and C entries of a tile.  Tiles 0-3 are the diagonal ones, so
+    // wave t < 4 produces the block it inverts next and reads back only its
+    // own writes: no workgroup barrier follows the Gram, and each wave goes on
+    // to its diagonal block or to phase A as soon as its own tiles are done.
+    // The planes are next read by other waves in the solve, after the barrier
+    // that closes phase A.
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-      const int tile = w + kWaves * jb;
+      if (jb == 1) {
+        load_s(0, kSHalf, kSChunks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int tile = jb == 0 ? w : (w == 4 || w == 5 ? w + 4 : 10);
       if (tile < 10) {
         const int I = kTileI[tile], J = kTileJ[tile];
         if (I < nmt) {
@@ -266,7 +278,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         }
       }
     }
-    __syncthreads();  // -G and C planes complete
   }
 
   // ---------------- Diagonal blocks: (I + G_tt)^-1 per 16-row tile --------
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   for (int kc0 = 0; kc0 < (kOne ? 1 : d_k); kc0 += SC::KC) {
     if (!kOne && kc0 > 0) {
       __syncthreads();  // every wave is done with the previous chunk
-      load_s(kc0);
+      load_s(kc0, 0, kSChunks);
       qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, kc0);
       qk_commit<DT>(stage, qkbuf);
       __syncthreads();

@@ -180,8 +180,8 @@ __device__ __forceinline__ void split_pair(const f32x4& a, const f32x4& b, bf16x
 }
 
 // The ten lower-triangle tiles (I >= J) of a 64x64 Gram product, computed in
-// the fused variant.
-__constant__ constexpr int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ constexpr int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// the fused variant: the four diagonal tiles first.
+__constant__ constexpr int kTileI[10] = {0, 1, 2, 3, 1, 2, 2, 3, 3, 3};
+__constant__ constexpr int kTileJ[10] = {0, 1, 2, 3, 0, 0, 1, 0, 1, 2};
 
 }  // namespace bole
