@@ -1,8 +1,10 @@
 """Throughput of closed-form tree verification for one GDN layer on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-tree preparation (topology + log-space gate products), the G/C factor producer,
-value-tiled verify and the accepted-path commit.  Default workload: 16 requests,
+tree preparation (topology + log-space gate products), the G/C factors,
+value-tiled verify and the accepted-path commit.  The default path runs the
+first three in one launch (bole_tree_verify), then the commit; --path fused
+and --path split time the three- and four-launch forms.  Default workload: 16 requests,
 64-node random trees (depth <= 12), 32 state heads, d_k = d_v = 128, bf16
 q/k/v with float32 gates and states.  Several independent input sets are
 rotated so the bytes touched per rotation exceed the 256 MB last-level cache.
@@ -28,11 +30,13 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-PROFILE_COUNTERS = os.path.join(PROFILES, "bole_factor_verify_target_counters.json")
+PROFILE_COUNTERS = os.path.join(PROFILES, "bole_tree_verify_target_counters.json")
+KERNEL_SOURCE_NAMES = ("verify.hip", "verify_tiles.h", "tree_topo.h", "common.h")
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_tree_amd", "csrc", f)
-                  for f in ("verify.hip", "verify_tiles.h", "common.h")]
-# the fused bf16 verify kernel the default step launches (name as rocprofv3 prints it)
-DOMINANT_KERNEL = "verify_kernel<1, true, true>"
+                  for f in KERNEL_SOURCE_NAMES]
+# the bf16 verify kernel with preparation inside, which the default step
+# launches (name as rocprofv3 prints it)
+DOMINANT_KERNEL = "verify_kernel<1, true, true, true>"
 
 
 def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
@@ -40,6 +44,22 @@ def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
     beta read once; O (token dtype) and U (float32) written once."""
     per_node = 2 * e * d_k + e * d_v + 8 + e * d_v + 4 * d_v
     return int(sum(H * (4 * d_k * d_v + T * per_node) for T in sizes))
+
+
+def tree_verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
+    """bole_tree_verify: the verify bytes (its log-gates g take the place of logP
+    as the second per-node-head float read) plus the preparation's own: parent
+    read, logP written per node and head, depth, anc and order written per node,
+    tree_depth per tree."""
+    return verify_algorithmic_bytes(sizes, H, d_k, d_v, e) + int(
+        sum(T * (4 * H + 4 + 16) + 4 for T in sizes))
+
+
+DOMINANT = {  # path -> (launch name, algorithmic bytes of one launch)
+    "tree": ("tree_verify", tree_verify_algorithmic_bytes),
+    "fused": ("factor_verify", verify_algorithmic_bytes),
+    "split": ("verify", verify_algorithmic_bytes),
+}
 
 
 def kernel_source_hash():
@@ -105,8 +125,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     f_fetch, f_write = calib_kib / copy_fetch, calib_kib / copy_write
     traffic = (fetch * f_fetch + write * f_write) * 1024.0
     cfg = W.CONFIGS["target"]
-    algo = np.mean([verify_algorithmic_bytes(W.make_forest(cfg, seed).sizes(), cfg.H, cfg.d_k,
-                                             cfg.d_v, 2) for seed in range(4)])
+    algo = np.mean([tree_verify_algorithmic_bytes(W.make_forest(cfg, seed).sizes(), cfg.H,
+                                                  cfg.d_k, cfg.d_v, 2) for seed in range(4)])
     rec = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": kernel_source_hash(),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [n_f, n_w], "copy_mib": calib_mib,
@@ -116,7 +136,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     with open(PROFILE_COUNTERS, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
-    md = ["# HBM traffic of `bole_factor_verify`, target workload (rocprofv3 --pmc)", "",
+    md = ["# HBM traffic of `bole_tree_verify`, target workload (rocprofv3 --pmc)", "",
           "Commands (one counter per pass; each pass first copies "
           f"{calib_mib} MiB device-to-device for the calibration):", "", "```",
           commands["fetch"], commands["write"], "```", "",
@@ -129,9 +149,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
           f"| HBM bytes per launch (scaled) | {traffic / 1e6:.1f} MB |",
           f"| algorithmic bytes per launch | {algo / 1e6:.1f} MB |",
           f"| ratio | {traffic / algo:.3f} |", "",
-          f"Kernel source hash: `{rec['kernel_source_hash']}` (verify.hip, verify_tiles.h, "
-          "common.h); bench.py reports `traffic` only while it matches."]
-    with open(os.path.join(PROFILES, "bole_factor_verify_target_counters.md"), "w") as fh:
+          f"Kernel source hash: `{rec['kernel_source_hash']}` ({', '.join(KERNEL_SOURCE_NAMES)}); "
+          "bench.py reports `traffic` only while it matches."]
+    with open(os.path.join(PROFILES, "bole_tree_verify_target_counters.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(rec))
 
@@ -206,6 +226,9 @@ def launch(s, bole, which):
     elif which == "verify":
         bole.bole_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C, t.order,
                          t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
+    elif which == "tree_verify":
+        bole.bole_tree_verify(s.q, s.k, s.v, t.parent, s.g[0], s.beta, s.pool, s.slot, t.tree_off,
+                              s.O, s.U, t.depth, t.anc, t.order, t.tree_depth, lp, s.rnd.err)
     elif which == "factor_verify":
         bole.bole_factor_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, t.anc, t.order,
                                 t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
@@ -217,14 +240,16 @@ def launch(s, bole, which):
 
 
 STEPS = {
-    # G/C produced and consumed in one launch (the default)
+    # preparation, G/C and verify in one launch, then the commit (the default)
+    "tree": ("tree_verify", "commit"),
+    # preparation on its own, G/C produced and consumed in one launch
     "fused": ("tree_prep", "factor_verify", "commit"),
     # the four-call path: G/C written by the producer, read back by verify
     "split": ("tree_prep", "factor_gc", "verify", "commit"),
 }
 
 
-def run_step(s, bole, path="fused"):
+def run_step(s, bole, path="tree"):
     """One pass of the whole path on the current stream."""
     for which in STEPS[path]:
         launch(s, bole, which)
@@ -328,8 +353,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="target", choices=sorted(W.CONFIGS))
     ap.add_argument("--sets", type=int, default=4, help="rotated independent input sets")
-    ap.add_argument("--path", default="fused", choices=sorted(STEPS),
-                    help="fused: prep + factor_verify + commit; split: the four calls")
+    ap.add_argument("--path", default="tree", choices=sorted(STEPS),
+                    help="tree: tree_verify + commit; fused: prep + factor_verify + commit; "
+                         "split: the four calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
@@ -369,8 +395,8 @@ def main():
     e = 2 if cfg.dtype == "bf16" else 4
 
     for i in range(args.warmup):
-        run_step(sets[i % len(sets)], bole, args.path)
-        run_step(sets[i % len(sets)], bole, "split")
+        for p in STEPS:
+            run_step(sets[i % len(sets)], bole, p)
     torch.cuda.synchronize()
     for s in sets:
         assert s.rnd.error_bits() == 0, "device error bits set"
@@ -379,7 +405,7 @@ def main():
     # replayed in rotation): launching three kernels per step from Python costs
     # more host time than the GPU spends on them.
     K = args.steps
-    other = "split" if args.path == "fused" else "fused"
+    others = [p for p in STEPS if p != args.path]
     R = 4 * len(sets)  # steps per rotation graph
     singles = [capture(torch, lambda s_=s_: run_step(s_, bole, args.path)) for s_ in sets]
     check_graph_replay(sets[0], singles[0], bole, args.path, torch)
@@ -403,12 +429,15 @@ def main():
         return e0.elapsed_time(e1) / k
 
     ms_step = time_k_steps(args.path, K, singles)
-    singles_other = [capture(torch, lambda s_=s_: run_step(s_, bole, other)) for s_ in sets]
-    ms_other = time_k_steps(other, max(K // 2, 10), singles_other)
+    ms_other = {}
+    for other in others:
+        singles_other = [capture(torch, lambda s_=s_, o_=other: run_step(s_, bole, o_))
+                         for s_ in sets]
+        ms_other[other] = time_k_steps(other, max(K // 2, 10), singles_other)
     ms_eager = time_steps_eager(sets, bole, args.path, max(K // 2, 10), torch)
     # per-kernel averages: each kernel alone, 4 x len(sets) launches per graph
     # over the rotated sets (same inputs, same stream)
-    kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "commit")
+    kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "tree_verify", "commit")
     avg = {}
     for which in kernels:
         n_in = 4 * len(sets)
@@ -417,13 +446,14 @@ def main():
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     for s_ in sets:
         assert s_.rnd.error_bits() == 0, "device error bits set"
-    dominant = "factor_verify" if args.path == "fused" else "verify"
+    dominant, bytes_fn = DOMINANT[args.path]
 
     nodes = sum(s.forest.N for s in sets) / len(sets)
     value = nodes * cfg.H / (ms_step * 1e-3)
-    vbytes = np.mean([verify_algorithmic_bytes(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
+    vbytes = np.mean([bytes_fn(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
     achieved = vbytes / (avg[dominant] * 1e-3) / 1e9
-    traffic = traffic_from_profile(kernel_source_hash())
+    # the committed counter record is the default path's dominant kernel
+    traffic = traffic_from_profile(kernel_source_hash()) if args.path == "tree" else None
 
     out = {
         "metric": "tree nodes x heads verified/sec per GDN layer",
@@ -445,7 +475,7 @@ def main():
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
             "nodes": nodes, "input_sets": len(sets), "path": args.path,
             "timing": "HIP graph replays: 16 captured steps per graph; kernels: 16 launches per graph",
-            "ms_per_step_other_path": {other: ms_other},
+            "ms_per_step_other_path": ms_other,
             "ms_per_step_eager_launches": ms_eager,
             "kernel_ms_back_to_back": avg,
         },

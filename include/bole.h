@@ -131,8 +131,10 @@ BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const f
  *
  * For each (tree b, head h, value tile r) it forms
  *     B0 = D_P Q S_pre^(r),  R = D_beta (V^(r) - D_P K S_pre^(r)),
- * propagates U = sum_{m=0..d_b} (-G)^m R with the d_b-step finite Neumann
- * recursion Z <- -G Z, U += Z (on chip), and reads out O^(r) = B0 + C U.
+ * U = (I + G)^-1 R (the value of the finite Neumann polynomial
+ * sum_{m=0..d_b} (-G)^m R, reached on chip by blocked forward substitution over
+ * 16-row tiles, each diagonal block inverted by its own Neumann series), and
+ * reads out O^(r) = B0 + C U.
  * All products run on bf16 MFMA with float32 accumulation; float32 operands
  * (states, G, C, Z, U, and float32 q/k) are split into bf16 hi+lo parts.
  *
@@ -173,6 +175,35 @@ BOLE_API int bole_factor_verify(int32_t dtype, const void* q, const void* k, con
                                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B,
                                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, void* O, float* U,
                                 uint32_t* err, void* stream);
+
+/*
+ * bole_tree_verify - bole_tree_prep (for one layer) and bole_factor_verify in
+ * one launch.  Each (tree, head) workgroup derives its tree's topology and its
+ * head's gate sums logP itself, with the arithmetic of bole_tree_prep (so they
+ * are bit-identical to it), and publishes them for bole_commit_path: depth,
+ * anc, order and tree_depth from head 0, logP from every head.  The
+ * per-round topology step and the per-layer gate preparation (arXiv page:
+ * the round's stages; review, Eq. 4 paragraph) then cost no launch of their
+ * own.
+ *
+ *  in   q, k, v, beta, state_pool, slot, tree_off, B, N, H, d_k, d_v
+ *                                    as bole_factor_verify
+ *  in   parent[N]                    local parent of each node, -1 for a root
+ *  in   log_gamma[N,H]               float32 log-gates g of this layer
+ *  out  O, U                         as bole_factor_verify
+ *  out  depth[N], anc[N], order[N], tree_depth[B], logP[N,H]
+ *                                    as bole_tree_prep (logP of this layer)
+ *  out  err                          BAD_PARENT, CYCLE, TREE_SIZE, BAD_SLOT
+ * A rejected tree gets tree_depth -1 and no O or U.  The d_k limit of
+ * bole_factor_verify applies.
+ */
+BOLE_API int bole_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                              const int32_t* parent, const float* log_gamma, const float* beta,
+                              const float* state_pool, int32_t n_slots, const int32_t* slot,
+                              const int32_t* tree_off, int32_t B, int32_t N, int32_t H,
+                              int32_t d_k, int32_t d_v, void* O, float* U, int32_t* depth,
+                              uint64_t* anc, int32_t* order, int32_t* tree_depth, float* logP,
+                              uint32_t* err, void* stream);
 
 /*
  * bole_commit_path - accepted-path state reconstruction for L layers in one

@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.bole_factor_verify.restype = ctypes.c_int
         L.bole_factor_verify.argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P]
                                          + [i32] * 5 + [P, P, P, P])
+        L.bole_tree_verify.restype = ctypes.c_int
+        L.bole_tree_verify.argtypes = ([i32, P, P, P, P, P, P, P, i32, P, P]
+                                       + [i32] * 5 + [P] * 9)
         L.bole_commit_path.restype = ctypes.c_int
         L.bole_commit_path.argtypes = [i32, P, i64, i32, P, i32, P, i64, P, i64, P, i64, P, P,
                                        P, i32, i32, i32, i32, i32, P, P]
@@ -258,6 +261,48 @@ def bole_factor_verify(q, k, v, logP, beta, state_pool, slot, anc, order, depth,
         _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(logP), _ptr(beta), _ptr(state_pool),
         state_pool.shape[0], _ptr(slot), _ptr(anc), _ptr(order), _ptr(depth), _ptr(tree_off),
         _ptr(tree_depth), B, N, H, d_k, d_v, _ptr(O), _ptr(U), _ptr(err), _stream(stream)))
+
+
+def bole_tree_verify(q, k, v, parent, log_gamma, beta, state_pool, slot, tree_off, O, U,
+                     depth, anc, order, tree_depth, logP, err=None, stream=None):
+    """bole_tree_prep (one layer) + bole_factor_verify in one launch; writes the
+    prep outputs (depth, anc, order, tree_depth, this layer's logP) as well."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    B = tree_off.shape[0] - 1
+    if tuple(k.shape) != (N, H, d_k) or tuple(v.shape[:2]) != (N, H):
+        raise ValueError("q, k, v shapes disagree")
+    _need(parent, "parent", torch.int32, 1)
+    _need(tree_off, "tree_off", torch.int32, 1)
+    for t, nm in ((log_gamma, "log_gamma"), (beta, "beta"), (logP, "logP")):
+        _need(t, nm, torch.float32, 2)
+        if tuple(t.shape) != (N, H):
+            raise ValueError(f"{nm} must be [N, H]")
+    _need(state_pool, "state_pool", torch.float32, 4)
+    if tuple(state_pool.shape[1:]) != (H, d_v, d_k):
+        raise ValueError("state_pool must be [n_slots, H, d_v, d_k]")
+    _need(slot, "slot", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 1)
+    _need(order, "order", torch.int32, 1)
+    _need(depth, "depth", torch.int32, 1)
+    _need(tree_depth, "tree_depth", torch.int32, 1)
+    if parent.shape[0] != N or anc.shape[0] != N or order.shape[0] != N or depth.shape[0] != N:
+        raise ValueError("parent, anc, order and depth need N entries")
+    _need(O, "O", v.dtype, 3)
+    _need(U, "U", torch.float32, 3)
+    if tuple(O.shape) != (N, H, d_v) or tuple(U.shape) != (N, H, d_v):
+        raise ValueError("O and U must be [N, H, d_v]")
+    if slot.shape[0] != B or tree_depth.shape[0] != B:
+        raise ValueError("slot and tree_depth need B entries")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_tree_verify", lib().bole_tree_verify(
+        _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(parent), _ptr(log_gamma), _ptr(beta),
+        _ptr(state_pool), state_pool.shape[0], _ptr(slot), _ptr(tree_off), B, N, H, d_k, d_v,
+        _ptr(O), _ptr(U), _ptr(depth), _ptr(anc), _ptr(order), _ptr(tree_depth), _ptr(logP),
+        _ptr(err), _stream(stream)))
 
 
 def _layer_view(t, name, inner_ndim):

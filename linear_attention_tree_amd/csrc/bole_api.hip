@@ -23,6 +23,11 @@ int bole_factor_verify_launch(int32_t, const void*, const void*, const void*, co
                               const uint64_t*, const int32_t*, const int32_t*, const int32_t*,
                               const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
                               float*, uint32_t*, hipStream_t);
+int bole_tree_verify_launch(int32_t, const void*, const void*, const void*, const int32_t*,
+                            const float*, const float*, const float*, int32_t, const int32_t*,
+                            const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                            float*, int32_t*, uint64_t*, int32_t*, int32_t*, float*, uint32_t*,
+                            hipStream_t);
 int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
@@ -109,6 +114,26 @@ int bole_factor_verify(int32_t dtype, const void* q, const void* k, const void* 
   return bole_factor_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, anc,
                                    order, depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U,
                                    err, (hipStream_t)stream);
+}
+
+int bole_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                     const int32_t* parent, const float* log_gamma, const float* beta,
+                     const float* state_pool, int32_t n_slots, const int32_t* slot,
+                     const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                     int32_t d_v, void* O, float* U, int32_t* depth, uint64_t* anc,
+                     int32_t* order, int32_t* tree_depth, float* logP, uint32_t* err,
+                     void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !v || !parent || !log_gamma || !beta || !state_pool || !slot || !tree_off ||
+      !O || !U || !depth || !anc || !order || !tree_depth || !logP)
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || B > (1 << 24) || !grid_ok(B, H, 4))
+    return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k > bole_factor_verify_max_dk(dtype))
+    return BOLE_E_UNSUPPORTED;
+  return bole_tree_verify_launch(dtype, q, k, v, parent, log_gamma, beta, state_pool, n_slots,
+                                 slot, tree_off, B, N, H, d_k, d_v, O, U, depth, anc, order,
+                                 tree_depth, logP, err, (hipStream_t)stream);
 }
 
 int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,

@@ -1,17 +1,12 @@
 // Round-level topology step and log-space gate products.
 //
-// Topology (arXiv page of Bole: ancestor mask; review, Lemma 3's depth d):
-// one wave64 per tree, one lane per node.  The ancestor-or-self set is built
-// by pointer jumping: after round s every lane knows the first 2^s nodes of
-// its upward path and the node 2^s steps up; six rounds cover any path of a
-// tree with at most 64 nodes, so a lane that still has a jump target after six
-// rounds lies on or leads into a cycle.
+// Topology: one wave64 per tree, one lane per node (tree_topo.h).
 //
 // Gate products (review, Eq. 4 paragraph: P_i multiplies the gates of i's
 // ancestors and of i): logP_i is the root-first running sum of g along the path
 // in float32, one rounding per add (so logP_i = logP_parent(i) + g_i exactly as
 // computed for the parent).
-#include "common.h"
+#include "tree_topo.h"
 
 namespace bole {
 
@@ -88,55 +83,23 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(
   }
 
   if (w == 0) {
-    const bool live = lane < T;
-    p = live ? p : -1;
-    const bool bad = live && p != -1 && (p < 0 || p >= T || p == lane);
-    uint32_t fail = 0;
-    int dmax = 0;
-    if (ballot64(bad)) {
-      fail = BOLE_ERR_BAD_PARENT;
-    } else {
-      // pointer jumping; a lane that can still jump after six rounds (64 nodes)
-      // lies on or leads into a cycle
-      uint64_t anc = live ? (1ull << lane) : 0ull;
-      int jmp = live ? p : -1;
-      for (int round = 0; round < 6 && ballot64(jmp >= 0); ++round) {
-        const int src = jmp >= 0 ? jmp : lane;
-        const uint64_t a2 = __shfl(anc, src);
-        const int j2 = __shfl(jmp, src);
-        if (jmp >= 0) {
-          anc |= a2;
-          jmp = j2;
+    const TreeTopo tp = tree_topology(lane, T, p);
+    const uint32_t fail = tp.fail;
+    const int dmax = tp.dmax;
+    if (!fail) {
+      if (lane < T) {
+        node_dep[lane] = tp.dep;
+        if (publish) {
+          depth_out[off + lane] = tp.dep;
+          anc_out[off + lane] = tp.anc;
+          order_out[off + tp.pos] = lane;
         }
-      }
-      if (ballot64(live && jmp >= 0)) {
-        fail = BOLE_ERR_CYCLE;
-      } else {
-        const int dep = live ? __popcll(anc) - 1 : -1;
-        if (live) node_dep[lane] = dep;
-        // stable sort by (depth, local id): rank = nodes on shallower levels plus
-        // lower ids on the same level.  Every level up to the deepest holds a
-        // node (a node's parent is one level up), so the scan ends at T.
-        int acc = 0, pos = 0, lev = 0;
-        for (; acc < T && lev < kMaxTree; ++lev) {
-          const uint64_t m = ballot64(dep == lev);
-          if (dep == lev) pos = acc + __popcll(m & ((1ull << lane) - 1ull));
-          acc += __popcll(m);
-        }
-        dmax = lev - 1;
-        if (live) {
-          if (publish) {
-            depth_out[off + lane] = dep;
-            anc_out[off + lane] = anc;
-            order_out[off + pos] = lane;
-          }
-          // path table: every ancestor-or-self j of this node at its depth
-          uint64_t m = anc;
-          while (m) {
-            const int j = __builtin_ctzll(m);
-            path[lane][node_dep[j]] = (uint8_t)j;
-            m &= m - 1ull;
-          }
+        // path table: every ancestor-or-self j of this node at its depth
+        uint64_t m = tp.anc;
+        while (m) {
+          const int j = __builtin_ctzll(m);
+          path[lane][node_dep[j]] = (uint8_t)j;
+          m &= m - 1ull;
         }
       }
     }

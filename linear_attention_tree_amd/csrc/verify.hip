@@ -30,6 +30,7 @@
 //           way, as 16-byte row pieces staged for the accumulator layout.
 #include <type_traits>
 
+#include "tree_topo.h"
 #include "verify_tiles.h"
 
 namespace bole {
@@ -38,8 +39,11 @@ namespace bole {
 // products and their masked epilogue run here, from the Q/K rows already staged
 // for the state contractions, with the same arithmetic as bole_factor_gc (d_k
 // must fit one staged chunk).  ONE: d_k fits one staged chunk (always so when
-// fused), which drops the re-staging loop and its registers.
-template <int DT, bool FUSED, bool ONE>
+// fused), which drops the re-staging loop and its registers.  PREP (fused only):
+// the kernel derives the tree's topology and this head's gate sums itself from
+// the parents and log-gates, with the arithmetic of bole_tree_prep, and
+// publishes them for the commit; the order/depth/anc/logP inputs are unused.
+template <int DT, bool FUSED, bool ONE, bool PREP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ logP, const float* __restrict__ beta,
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int32_t* __restrict__ order,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ tree_off,
     const int32_t* __restrict__ tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
-    int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf,
+    int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf, PrepIO prep,
     uint32_t* __restrict__ err) {
   using SC = StageCfg<DT>;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::LROW];
@@ -60,6 +64,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   __shared__ int rowDep[kMaxTree];
   __shared__ __align__(16) int rowNode[kMaxTree];
   __shared__ bf16x4 invs[4][2][64];  // (I + G_tt)^-1, A layout, hi / lo
+  __shared__ int tree_ok;
 
   const int NV = (d_v + kBV - 1) / kBV;
   const int lid = xcd_remap(blockIdx.x, B * H * NV);
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 
   // independent per-tree scalars, fetched together
   const int off = tree_off[b], end = tree_off[b + 1];
-  const int td = tree_depth[b];
+  const int td = PREP ? 0 : tree_depth[b];
   const int s = slot[b];
   const int T = end - off;
   if (off < 0 || end > N || T < 1 || T > kMaxTree) {
@@ -89,8 +94,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // tree and values masked afterwards): a load behind a divergent branch makes
   // the wait for it conservative, and it would then wait for every load issued
   // after it as well.
-  // level-order rows: row p holds node order[p]
-  const int ord = order[off + min(lane, T - 1)];
+  // level-order rows: row p holds node order[p].  With PREP wave 0 fetches
+  // what the topology and the row tables are built from instead.
+  const int nl = off + min(lane, T - 1);
+  const int ord = PREP ? 0 : order[nl];
+  int p_raw = -1;
+  float g_raw = 0.0f, bt_raw = 0.0f;
+  if (PREP && w == 0) {  // uniform
+    p_raw = prep.parent[nl];
+    g_raw = prep.g[(int64_t)nl * H + h];
+    bt_raw = beta[(int64_t)nl * H + h];
+  }
   // G and C depend on the unit only: their loads go out first and are parked in
   // LDS once the operands below are in flight.  The fused variant clears the
   // planes instead (tiles above the diagonal are read and must be zero).
@@ -113,17 +127,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
 
   const int node_l = lane < T ? clamp_node(ord, T) : 0;
-  if (threadIdx.x < kMaxTree) {
+  u16x8 qkbuf[QkCfg<DT>::PER];
+  if (PREP) {
+    // the Q/K rows go out now, in node order, behind wave 0's small loads;
+    // the topology is derived while they stream in
+    qk_issue<DT, true>(qkbuf, q, k, nullptr, T, off, H, h, d_k, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (w == 0) {
+      // tree preparation for this (tree, head): topology (tree_topo.h), then
+      // logP level by level, logP_i = logP_parent(i) + g_i from +0 at the roots:
+      // the float32 adds of bole_tree_prep's root-first running sum, in order
+      const TreeTopo tp = tree_topology(lane, T, p_raw);
+      const bool row_in = lane < T;
+      if (!tp.fail) {
+        float lp = 0.0f;
+        for (int lev = 0; lev <= tp.dmax; ++lev) {
+          const float lpp = __shfl(lp, max(p_raw, 0));
+          if (tp.dep == lev) lp = __fadd_rn(lev == 0 ? 0.0f : lpp, g_raw);
+        }
+        // row tables at the node's level position (rows past the tree hold
+        // node 0 with zero scalars)
+        const int pos = tp.pos;
+        rowNode[pos] = row_in ? lane : 0;
+        posOf[lane] = pos;
+        const uint32_t rk = keep(row_in);
+        rowP[pos] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, expf(lp)) & rk);
+        rowBeta[pos] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & rk);
+        rowE2[pos] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, lp * kLog2e) & rk);
+        rowDep[pos] = row_in ? tp.dep : 0x7fff;
+        uint64_t m = tp.anc, apos = 0ull;  // ancestors in level positions
+        while (m) {
+          apos |= 1ull << posOf[__builtin_ctzll(m)];
+          m &= m - 1ull;
+        }
+        rowApos[pos] = apos;
+        if (row_in && r == 0) {
+          prep.logP[(int64_t)(off + lane) * H + h] = lp;
+          if (h == 0) {
+            prep.depth[off + lane] = tp.dep;
+            prep.anc[off + lane] = tp.anc;
+            prep.order[off + pos] = lane;
+          }
+        }
+      }
+      if (lane == 0) {
+        tree_ok = !tp.fail;
+        if (h == 0 && r == 0) {
+          prep.tree_depth[b] = tp.fail ? -1 : tp.dmax;
+          if (tp.fail) report(err, tp.fail);
+        }
+      }
+    }
+  } else if (threadIdx.x < kMaxTree) {
     rowNode[threadIdx.x] = node_l;
     if (lane < T) posOf[node_l] = lane;
   }
-  __syncthreads();  // rowNode visible
+  __syncthreads();  // rowNode visible (and with PREP every row table)
+  if (PREP && !tree_ok) return;  // uniform: a rejected tree
 
   // everything below depends on the rows only.  Issue order: the Q/K rows
   // (needed first), the row scalars (wave 0), then the state slice and V,
   // which are consumed last.
-  u16x8 qkbuf[QkCfg<DT>::PER];
-  qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, 0);
+  if (!PREP) qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, 0);
 
   // S_pre rows of this wave's 16 value columns: first chunk's B fragments
   const int vloc = 16 * w + l16;
@@ -156,7 +221,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat) * kGcPlane + o) = hi;
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat + 1) * kGcPlane + o) = lo;
   }
-  if (w == 0) {
+  if (!PREP && w == 0) {
     // The row tables are built by one wave: each row-scalar load touches 64
     // different cache lines (the rows are H elements apart), so eight copies
     // would crowd the address units while the Q/K rows stream in.  Rows past
@@ -185,7 +250,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     // depth of level-order row `lane` (nondecreasing in the row index)
     rowDep[lane] = row_in ? dep_raw : 0x7fff;
   }
-  qk_commit<DT>(stage, qkbuf);  // waits for the Q/K rows
+  if (PREP)
+    qk_commit<DT, true>(stage, qkbuf, posOf, T);  // waits for the Q/K rows
+  else
+    qk_commit<DT>(stage, qkbuf);
   __syncthreads();  // staged rows and row tables visible
   // The state slice and V are requested only once the workgroup's Q/K rows are
   // in: the memory system serves concurrent requests interleaved, so issued
@@ -555,22 +623,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 }  // namespace bole
 
 namespace {
-template <int DT, bool FUSED, bool ONE>
+template <int DT, bool FUSED, bool ONE, bool PREP = false>
 int launch_verify_t(const void* q, const void* k, const void* v, const float* logP,
                     const float* beta, const float* state_pool, int32_t n_slots,
                     const int32_t* slot, const float* G, const float* C, const uint64_t* anc,
                     const int32_t* order, const int32_t* depth, const int32_t* tree_off,
                     const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
-                    int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s) {
+                    int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s,
+                    bole::PrepIO prep = bole::PrepIO{}) {
   const int NV = (d_v + bole::kBV - 1) / bole::kBV;
   const dim3 grid(B * H * NV), block(bole::kThreads);
   const int esize = DT == BOLE_BF16 ? 2 : 4;
   const bool v_ok = d_v % (16 / esize) == 0 && (uintptr_t)v % 16 == 0;
   const bool out_ok = d_v % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)O % (4 * esize) == 0;
   const int vecf = (v_ok ? bole::kVecV : 0) | (out_ok ? bole::kVecOut : 0);
-  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE>), grid, block, 0, s, q, k, v, logP,
-                     beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, err);
+  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP>), grid, block, 0, s, q, k, v,
+                     logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
+                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err);
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 
@@ -624,4 +693,23 @@ extern "C" int bole_factor_verify_launch(int32_t dtype, const void* q, const voi
   return launch_verify<true>(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, nullptr,
                              nullptr, anc, order, depth, tree_off, tree_depth, B, N, H, d_k, d_v,
                              O, U, err, s);
+}
+
+extern "C" int bole_tree_verify_launch(int32_t dtype, const void* q, const void* k, const void* v,
+                                       const int32_t* parent, const float* log_gamma,
+                                       const float* beta, const float* state_pool,
+                                       int32_t n_slots, const int32_t* slot,
+                                       const int32_t* tree_off, int32_t B, int32_t N, int32_t H,
+                                       int32_t d_k, int32_t d_v, void* O, float* U,
+                                       int32_t* depth, uint64_t* anc, int32_t* order,
+                                       int32_t* tree_depth, float* logP, uint32_t* err,
+                                       hipStream_t s) {
+  const bole::PrepIO prep{parent, log_gamma, depth, anc, order, tree_depth, logP};
+  if (dtype == BOLE_BF16)
+    return launch_verify_t<BOLE_BF16, true, true, true>(
+        q, k, v, nullptr, beta, state_pool, n_slots, slot, nullptr, nullptr, nullptr, nullptr,
+        nullptr, tree_off, nullptr, B, N, H, d_k, d_v, O, U, err, s, prep);
+  return launch_verify_t<BOLE_F32, true, true, true>(
+      q, k, v, nullptr, beta, state_pool, n_slots, slot, nullptr, nullptr, nullptr, nullptr,
+      nullptr, tree_off, nullptr, B, N, H, d_k, d_v, O, U, err, s, prep);
 }

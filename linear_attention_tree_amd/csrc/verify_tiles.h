@@ -48,6 +48,18 @@ __device__ __forceinline__ int vtile_idx(int row, int col) {
   return row * kBV + (col ^ (((row >> 2) & 3) << 4));
 }
 
+// Tree preparation done inside the verify kernel (bole_tree_verify): its
+// inputs and the outputs it publishes for the commit.
+struct PrepIO {
+  const int32_t* parent;  // [N] local parent, -1 for a root
+  const float* g;         // [N, H] log-gates of the layer
+  int32_t* depth;         // [N]
+  uint64_t* anc;          // [N]
+  int32_t* order;         // [N]
+  int32_t* tree_depth;    // [B]
+  float* logP;            // [N, H] of the layer
+};
+
 // Bit flags of the value-tile transfers, set by the host.
 // kVecV: d_v is a multiple of the elements in 16 bytes of v and v is 16-byte
 // aligned, so V rows move as 16-byte pieces.  kVecOut: d_v % 4 == 0 and U and O
@@ -73,7 +85,10 @@ struct QkCfg {
   static constexpr int PER = 2 * kMaxTree * PIECES / kThreads;
 };
 
-template <int DT>
+// NODE_ORDER: the rows are fetched in node order (piece row n holds node n), so
+// the loads need only the tree's offset; qk_commit then stores node n at its
+// level position posOf[n] (positions past the tree keep their index).
+template <int DT, bool NODE_ORDER = false>
 __device__ __forceinline__ void qk_issue(u16x8* buf, const void* q, const void* k,
                                          const int* rowNode, int T, int off, int H, int h,
                                          int d_k, int kc0) {
@@ -87,7 +102,8 @@ __device__ __forceinline__ void qk_issue(u16x8* buf, const void* q, const void* 
     const int kk = kc0 + QC::EPP * pc;
     // unconditional load (row and column clamped into the tree), zeroed after
     const bool in = row < T && kk < d_k;
-    const int64_t e = ((int64_t)(off + rowNode[min(row, T - 1)]) * H + h) * d_k + (kk < d_k ? kk : 0);
+    const int node = NODE_ORDER ? min(row, T - 1) : rowNode[min(row, T - 1)];
+    const int64_t e = ((int64_t)(off + node) * H + h) * d_k + (kk < d_k ? kk : 0);
     const u16x8 val =
         DT == BOLE_BF16
             ? *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(mat == 0 ? q : k) + e)
@@ -97,8 +113,9 @@ __device__ __forceinline__ void qk_issue(u16x8* buf, const void* q, const void* 
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void qk_commit(__bf16* stage, const u16x8* buf) {
+template <int DT, bool NODE_ORDER = false>
+__device__ __forceinline__ void qk_commit(__bf16* stage, const u16x8* buf,
+                                          const int* posOf = nullptr, int T = 0) {
   using SC = StageCfg<DT>;
   using QC = QkCfg<DT>;
 #pragma unroll
@@ -106,7 +123,8 @@ __device__ __forceinline__ void qk_commit(__bf16* stage, const u16x8* buf) {
     const int id = threadIdx.x + kThreads * it;
     const int mat = id / (kMaxTree * QC::PIECES);
     const int rem = id - mat * (kMaxTree * QC::PIECES);
-    const int row = rem / QC::PIECES, pc = rem - (rem / QC::PIECES) * QC::PIECES;
+    const int r0 = rem / QC::PIECES, pc = rem - (rem / QC::PIECES) * QC::PIECES;
+    const int row = NODE_ORDER && r0 < T ? posOf[r0] & (kMaxTree - 1) : r0;
     if (DT == BOLE_BF16) {
       *reinterpret_cast<u16x8*>(stage + (mat * kMaxTree + row) * SC::LROW + 8 * swz<DT>(row, pc)) =
           buf[it];

@@ -1,4 +1,4 @@
-"""Device-buffer plumbing around the four calls of libbole.
+"""Device-buffer plumbing around the calls of libbole.
 
 ``TreeRound`` owns the per-round topology buffers of one packed forest and the
 per-layer G/C workspace, allocates outputs with PyTorch and issues the calls in
@@ -94,6 +94,24 @@ class TreeRound:
         bole.bole_factor_verify(q, k, v, logP, beta, state_pool, slot, t.anc, t.order, t.depth,
                                 t.tree_off, t.tree_depth, O, U, self.err, stream)
         return O, U
+
+    def tree_layer(self, q, k, v, log_gamma, beta, state_pool, slot, O=None, U=None,
+                   logP=None, stream=None):
+        """Tree preparation for this layer and the fused verify in one launch
+        (bole_tree_verify).  Fills the topology buffers; returns O, U and the
+        layer's logP [N, H]."""
+        t = self.topo
+        N, H, _ = q.shape
+        d_v = v.shape[2]
+        if O is None:
+            O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
+        if U is None:
+            U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
+        if logP is None:
+            logP = torch.empty(N, H, dtype=torch.float32, device=v.device)
+        bole.bole_tree_verify(q, k, v, t.parent, log_gamma, beta, state_pool, slot, t.tree_off, O,
+                              U, t.depth, t.anc, t.order, t.tree_depth, logP, self.err, stream)
+        return O, U, logP
 
     def commit(self, state_pool, slot, k, U, logP, accept, stream=None):
         t = self.topo

@@ -131,12 +131,15 @@ def offset_copy(t, dtype=None):
     return view
 
 
-def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, misalign=False):
+def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, misalign=False,
+              tree=False):
     """Run prep, factor, verify (and commit) on the GPU through the C ABI.
 
-    misalign: v, O and U live one element past an aligned address (the kernels'
-    element-wise fallbacks).  Returns dict with per-layer O, U (numpy float64),
-    the state pools after commit, the prep outputs and the error word."""
+    fused: bole_factor_verify after bole_tree_prep; tree: bole_tree_verify per
+    layer (preparation inside the verify launch).  misalign: v, O and U live one
+    element past an aligned address (the kernels' element-wise fallbacks).
+    Returns dict with per-layer O, U (numpy float64), the state pools after
+    commit, the prep outputs and the error word."""
     import torch
     from linear_attention_tree_amd import TreeRound
     f = case.forest
@@ -144,7 +147,7 @@ def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, 
     rnd = TreeRound(f.parent, f.tree_off, case.cfg.H, device=device)
     dev = [to_dev(case, l, device) for l in layers]
     g_all = torch.stack([d["g"] for d in dev])
-    logP = rnd.prep(g_all)
+    logP = torch.empty_like(g_all) if tree else rnd.prep(g_all)
     slot = torch.from_numpy(case.slot).to(device)
     pools = torch.stack([torch.from_numpy(case.S_pre[l]) for l in layers]).to(device)
     Os, Us = [], []
@@ -154,8 +157,12 @@ def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, 
             v = offset_copy(v)
             O = offset_copy(torch.empty_like(v))
             U = offset_copy(torch.empty(v.shape, dtype=torch.float32, device=v.device))
-        O, U = rnd.layer(d["q"], d["k"], v, logP[li], d["beta"], pools[li], slot, O=O, U=U,
-                         fused=fused)
+        if tree:
+            O, U, _ = rnd.tree_layer(d["q"], d["k"], v, d["g"], d["beta"], pools[li], slot, O=O,
+                                     U=U, logP=logP[li])
+        else:
+            O, U = rnd.layer(d["q"], d["k"], v, logP[li], d["beta"], pools[li], slot, O=O, U=U,
+                             fused=fused)
         Os.append(O)
         Us.append(U)
     out = dict(logP=logP.cpu().numpy(), depth=rnd.topo.depth.cpu().numpy(),

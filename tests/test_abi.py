@@ -33,15 +33,16 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_symbols()
     assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
-                          "bole_verify", "bole_factor_verify", "bole_commit_path",
-                          "bole_status_string"}
+                          "bole_verify", "bole_factor_verify", "bole_tree_verify",
+                          "bole_commit_path", "bole_status_string"}
     for n in names:
         assert hasattr(L, n), n
         assert hasattr(lat, n), n   # same names in the Python binding
 
 
 def test_internal_launchers_are_hidden(L):
-    for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch"):
+    for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch",
+              "bole_tree_verify_launch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
 
@@ -102,6 +103,23 @@ def test_factor_verify_argument_errors(L):
     assert call(dk=256) == E_UNSUPPORTED          # one staged chunk only
     assert call(dtype=0, dk=128) == E_UNSUPPORTED
     assert call(dtype=0, dk=64, dv=24) == E_UNSUPPORTED
+
+
+def test_tree_verify_argument_errors(L):
+    f = L.bole_tree_verify
+
+    def call(dtype=1, dk=128, dv=128, parent=FAKE, logP=FAKE, B=1, H=1):
+        return f(dtype, FAKE, FAKE, FAKE, parent, FAKE, FAKE, FAKE, 1, FAKE, FAKE, B, 1, H, dk, dv,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, logP, None, None)
+
+    assert call(dtype=3) == E_DTYPE
+    assert call(parent=None) == E_NULL
+    assert call(logP=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(H=0) == E_SHAPE
+    assert call(dk=256) == E_UNSUPPORTED
+    assert call(dtype=0, dk=128) == E_UNSUPPORTED
+    assert call(dv=40) == E_UNSUPPORTED
 
 
 def test_commit_argument_errors(L):

@@ -5,7 +5,8 @@ partial 64-wide commit blocks), single-node trees, a 64-node chain (the deepest
 path a tree can hold), trees with several roots, beta = 0 and gates whose
 products underflow float32.  Both the two-call path (bole_factor_gc +
 bole_verify) and the fused bole_factor_verify run where the latter supports
-the shape.  Same bars as the main parity tests.
+the shape, and so does bole_tree_verify (preparation inside the launch).  Same
+bars as the main parity tests.
 """
 
 import sys
@@ -47,9 +48,9 @@ def fused_ok(cfg):
     return cfg.d_k <= (128 if cfg.dtype == "bf16" else 64)
 
 
-def check(case, fused, label, misalign=False):
+def check(case, fused, label, misalign=False, tree=False):
     tol = tolerance(case.cfg)
-    out = gpu_round(case, fused=fused, misalign=misalign)
+    out = gpu_round(case, fused=fused, misalign=misalign, tree=tree)
     assert out["err"] == 0
     O, U, S_new = oracle_layer(case, 0)
     f = case.forest
@@ -57,7 +58,8 @@ def check(case, fused, label, misalign=False):
     eo = block_rel_err(out["O"][0], O, f.tree_off)
     eu = block_rel_err(out["U"][0], U, f.tree_off)
     es = state_rel_err(out["S"][0], S_new, case.slot, units)
-    say(f"  {label}{' fused' if fused else ''}: O {eo:.2e}  U {eu:.2e}  S_new {es:.2e}")
+    say(f"  {label}{' tree' if tree else ' fused' if fused else ''}: O {eo:.2e}  U {eu:.2e}  "
+        f"S_new {es:.2e}")
     assert np.all(np.isfinite(out["O"][0])) and np.all(np.isfinite(out["U"][0]))
     assert eo <= tol and eu <= tol and es <= tol
     return out
@@ -75,6 +77,7 @@ def test_head_dims(dtype, d_k, d_v):
     check(case, False, "split")
     if fused_ok(cfg):
         check(case, True, "split")
+        check(case, True, "split", tree=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -88,6 +91,7 @@ def test_chain_of_64(dtype):
     say(f"chain of 64 {dtype}")
     check(case, False, "split")
     check(case, True, "split")
+    check(case, True, "split", tree=True)
 
 
 def test_several_roots():
@@ -99,6 +103,7 @@ def test_several_roots():
     say("several roots")
     check(case, False, "split")
     check(case, True, "split")
+    check(case, True, "split", tree=True)
 
 
 def test_beta_zero():
@@ -120,6 +125,7 @@ def test_gate_products_underflow():
     say("gate products underflow")
     check(case, False, "split")
     check(case, True, "split")
+    check(case, True, "split", tree=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -131,3 +137,4 @@ def test_unaligned_token_buffers(dtype):
     say(f"unaligned token buffers {dtype}")
     check(case, False, "split", misalign=True)
     check(case, True, "split", misalign=True)
+    check(case, True, "split", misalign=True, tree=True)

@@ -340,16 +340,18 @@ def test_factor_verify_bit_identical_to_two_calls(cases, name):
 # ---------------------------------------------------------------------------
 # HIP graph capture
 
+@pytest.mark.parametrize("path", ["fused", "tree"])
 @pytest.mark.parametrize("name", ["decode", "target"])
-def test_graph_replay_matches_eager(cases, name):
-    """The whole step (prep, fused factor + verify, commit) captured in a HIP
-    graph reproduces the eager launches bit for bit, replay after replay, with
-    eager work and synchronizations between the replays."""
+def test_graph_replay_matches_eager(cases, name, path):
+    """The whole step (prep, fused factor + verify, commit; or tree_verify then
+    the commit) captured in a HIP graph reproduces the eager launches bit for
+    bit, replay after replay, with eager work and synchronizations between the
+    replays."""
     from linear_attention_tree_amd import TreeRound, bole
     from helpers import to_dev
     case = get_case(cases, name, n_layers=1)
     f = case.forest
-    say(f"graph replay {name}")
+    say(f"graph replay {name} {path}")
     d = to_dev(case, 0)
     rnd = TreeRound(f.parent, f.tree_off, case.cfg.H)
     t = rnd.topo
@@ -363,10 +365,16 @@ def test_graph_replay_matches_eager(cases, name):
     U = torch.empty(f.N, case.cfg.H, case.cfg.d_v, dtype=torch.float32, device="cuda")
 
     def step():
-        bole.bole_tree_prep(t.parent, t.tree_off, g, t.depth, t.anc, t.order, t.tree_depth,
-                            logP, rnd.err)
-        bole.bole_factor_verify(d["q"], d["k"], d["v"], logP[0], d["beta"], pool, slot, t.anc,
-                                t.order, t.depth, t.tree_off, t.tree_depth, O, U, rnd.err)
+        if path == "tree":
+            bole.bole_tree_verify(d["q"], d["k"], d["v"], t.parent, g[0], d["beta"], pool, slot,
+                                  t.tree_off, O, U, t.depth, t.anc, t.order, t.tree_depth,
+                                  logP[0], rnd.err)
+        else:
+            bole.bole_tree_prep(t.parent, t.tree_off, g, t.depth, t.anc, t.order, t.tree_depth,
+                                logP, rnd.err)
+            bole.bole_factor_verify(d["q"], d["k"], d["v"], logP[0], d["beta"], pool, slot,
+                                    t.anc, t.order, t.depth, t.tree_off, t.tree_depth, O, U,
+                                    rnd.err)
         bole.bole_commit_path(pool, slot, d["k"], U, logP[0], t.anc, t.tree_off, accept,
                               rnd.err)
 
