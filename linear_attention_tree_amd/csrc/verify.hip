@@ -140,14 +140,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       const TreeTopo tp = tree_topology(lane, T, p_raw);
       const bool row_in = lane < T;
       if (!tp.fail) {
+        // the ancestor-or-self set in level positions follows the same
+        // recursion, apos_i = apos_parent(i) | bit(pos_i), in the same rounds
+        const int pos = tp.pos;
+        const int src = max(p_raw, 0);
         float lp = 0.0f;
+        uint64_t apos = 0ull;
         for (int lev = 0; lev <= tp.dmax; ++lev) {
-          const float lpp = __shfl(lp, max(p_raw, 0));
-          if (tp.dep == lev) lp = __fadd_rn(lev == 0 ? 0.0f : lpp, g_raw);
+          const float lpp = __shfl(lp, src);
+          const uint64_t app = __shfl(apos, src);
+          if (tp.dep == lev) {
+            lp = __fadd_rn(lev == 0 ? 0.0f : lpp, g_raw);
+            apos = (lev == 0 ? 0ull : app) | (1ull << pos);
+          }
         }
         // row tables at the node's level position (rows past the tree hold
         // node 0 with zero scalars)
-        const int pos = tp.pos;
         rowNode[pos] = row_in ? lane : 0;
         posOf[lane] = pos;
         const uint32_t rk = keep(row_in);
@@ -155,12 +163,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         rowBeta[pos] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, bt_raw) & rk);
         rowE2[pos] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, lp * kLog2e) & rk);
         rowDep[pos] = row_in ? tp.dep : 0x7fff;
-        uint64_t m = tp.anc, apos = 0ull;  // ancestors in level positions
-        while (m) {
-          apos |= 1ull << posOf[__builtin_ctzll(m)];
-          m &= m - 1ull;
-        }
-        rowApos[pos] = apos;
+        rowApos[pos] = apos;  // zero past the tree
         if (row_in && r == 0) {
           prep.logP[(int64_t)(off + lane) * H + h] = lp;
           if (h == 0) {
