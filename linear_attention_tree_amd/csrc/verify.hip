@@ -24,7 +24,9 @@
 //  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
 //           a permuted K order (load_tri_blocks) that makes the lane's own U
 //           tiles the B operand: U never leaves registers.
-//  Readout  O = B0 + C U.  Every operand is split hi + lo, float32 accumulation.
+//  Readout  O = B0 + C U, float32 accumulation.  Products that U and the
+//           committed state depend on split every float32 operand hi + lo; O's
+//           own (Q S_pre, C U) do so only for float32 tokens (kOExact).
 //  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
 //           leave as 4-element pieces of the nodes' rows; V arrives the same
 //           way, as 16-byte row pieces staged for the accumulator layout.
@@ -55,6 +57,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf, PrepIO prep,
     uint32_t* __restrict__ err) {
   using SC = StageCfg<DT>;
+  // O's own products (Q S_pre for B0, C U) carry the split low halves only for
+  // float32 tokens; with bf16 tokens O is stored in bf16, and each product is
+  // taken at that precision (hi parts: relative error near 2^-8, inside the
+  // 2e-2 bar with a 2.5x margin).  Everything U and the committed state depend
+  // on keeps the split products.
+  constexpr bool kOExact = DT == BOLE_F32;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::LROW];
   // planes: -G hi, -G lo, C hi, C lo
   __shared__ __align__(16) __bf16 gcs[4 * kGcPlane];
@@ -465,8 +473,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
           const int ro = row * SC::LROW + 8 * swz<DT>(row, 4 * kk + g4);
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(stage + ro);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::LROW + ro);
+          // kOExact: B0 = D_P Q S feeds only O; with bf16 tokens O is stored in
+          // bf16 and S's low half is left out of Q S (K S, which feeds U and
+          // the committed state, keeps it)
           qs[mt] = mfma_bf16(aq, b_hi, qs[mt]);
-          qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
+          if (kOExact) qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
           ks[mt] = mfma_bf16(ak, b_hi, ks[mt]);
           ks[mt] = mfma_bf16(ak, b_lo, ks[mt]);
           if (DT == BOLE_F32) {
@@ -563,10 +574,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int J = 0; J <= I / 2; ++J) {
       const int o = gc_frag(16 * I + l16, J, g4);
       const bf16x8 ch = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
-      const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
       acc = mfma_bf16(ch, uh[J], acc);
-      acc = mfma_bf16(cl, uh[J], acc);
-      acc = mfma_bf16(ch, ul[J], acc);
+      if (kOExact) {  // bf16 tokens: C U at the precision O is stored in
+        const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
+        acc = mfma_bf16(cl, uh[J], acc);
+        acc = mfma_bf16(ch, ul[J], acc);
+      }
     }
     qs[I] = acc;
   }
