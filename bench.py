@@ -346,6 +346,162 @@ def cpu_baseline(cfg, seed, budget_s=12.0):
                       f"{f.N} nodes x {cfg.H} heads, float64) in {el:.1f} s"}
 
 
+def commit_algorithmic_bytes(forest, L, H, d_k, d_v, e):
+    """Compulsory HBM bytes of one commit over L layers: every committed slot
+    read and written once (float32), plus the accepted path's key and U rows."""
+    depth = np.zeros(forest.N, np.int64)
+    for b in range(forest.B):
+        o = forest.tree_off[b]
+        for i in range(forest.tree_off[b + 1] - o):  # parents precede children or not: walk up
+            j, d = i, 0
+            while forest.parent[o + j] >= 0:
+                j, d = forest.parent[o + j], d + 1
+            depth[o + i] = d
+    path_len = [int(depth[forest.tree_off[b] + a]) + 1
+                for b, a in enumerate(forest.accept) if a >= 0]
+    per_head = sum(8 * d_k * d_v + la * (e * d_k + 4 * d_v) for la in path_len)
+    return L * H * per_head
+
+
+def build_states_device(cfg, B, layer, seed, torch, TreeRound, dev):
+    """As build_states_on_gpu, with the prefix tokens drawn on the device."""
+    pre = W.device_prefix(cfg, B, layer, seed, torch, dev)
+    pool = torch.zeros(B, cfg.H, cfg.d_v, cfg.d_k, dtype=torch.float32, device=dev)
+    slot = torch.arange(B, dtype=torch.int32, device=dev)
+    P, done = cfg.prefix, 0
+    while done < P:
+        T = min(64, P - done)
+        f = W.chain_forest(B, T)
+        rnd = TreeRound(f.parent, f.tree_off, cfg.H, device=dev)
+
+        def tok(a):  # [P, B, H, ...] -> [B*T, H, ...], tree-major
+            return a[done:done + T].transpose(0, 1).reshape(B * T, *a.shape[2:]).contiguous()
+
+        q, k, v, g, beta = tok(pre.q), tok(pre.k), tok(pre.v), tok(pre.g), tok(pre.beta)
+        logP = rnd.prep(g[None])[0]
+        _, U = rnd.layer(q, k, v, logP, beta, pool, slot)
+        rnd.commit(pool[None], slot, k[None], U[None], logP[None], f.accept)
+        done += T
+    return pool
+
+
+def round_main(cfg, args, torch, TreeRound, bole, dev):
+    """One step = one verification round over cfg.L layers: the per-layer
+    verify launches, then one commit over all layers (in place, so each round
+    verifies against the states the previous round committed)."""
+    if args.path == "split":
+        raise SystemExit("the multi-layer round runs --path tree or --path fused")
+    L, H = cfg.L, cfg.H
+    f = W.make_forest(cfg, 0)
+    B, N = f.B, f.N
+    x = W.device_layer(cfg, N, 0, 0, torch, dev, lead=(L,))
+    pool = torch.stack([build_states_device(cfg, B, l, 0, torch, TreeRound, dev)
+                        for l in range(L)])
+    slot = torch.arange(B, dtype=torch.int32, device=dev)
+    accept = torch.from_numpy(f.accept).to(dev)
+    rnd = TreeRound(f.parent, f.tree_off, H, device=dev)
+    t = rnd.topo
+    logP = torch.empty(L, N, H, dtype=torch.float32, device=dev)
+    O = torch.empty(L, N, H, cfg.d_v, dtype=x.v.dtype, device=dev)
+    U = torch.empty(L, N, H, cfg.d_v, dtype=torch.float32, device=dev)
+
+    def verify_layers(path):
+        if path == "tree":
+            for l in range(L):
+                bole.bole_tree_verify(x.q[l], x.k[l], x.v[l], t.parent, x.g[l], x.beta[l],
+                                      pool[l], slot, t.tree_off, O[l], U[l], t.depth, t.anc,
+                                      t.order, t.tree_depth, logP[l], rnd.err)
+        else:
+            bole.bole_tree_prep(t.parent, t.tree_off, x.g, t.depth, t.anc, t.order,
+                                t.tree_depth, logP, rnd.err)
+            for l in range(L):
+                bole.bole_factor_verify(x.q[l], x.k[l], x.v[l], logP[l], x.beta[l], pool[l],
+                                        slot, t.anc, t.order, t.depth, t.tree_off, t.tree_depth,
+                                        O[l], U[l], rnd.err)
+
+    def commit():
+        bole.bole_commit_path(pool, slot, x.k, U, logP, t.anc, t.tree_off, accept, rnd.err)
+
+    def one_round(path):
+        verify_layers(path)
+        commit()
+
+    for _ in range(max(args.warmup, 1)):
+        for p in ("tree", "fused"):
+            one_round(p)
+    torch.cuda.synchronize()
+    assert rnd.error_bits() == 0, "device error bits set"
+    K = args.steps
+    graphs = {p: capture(torch, lambda p_=p: one_round(p_)) for p in ("tree", "fused")}
+    ms_round = {p: time_graphs([g], K, torch) for p, g in graphs.items()}
+    g_ver = capture(torch, lambda: verify_layers(args.path))
+    ms_verify = time_graphs([g_ver], max(K // 4, 5), torch)
+    g_com = capture(torch, commit)
+    ms_commit = time_graphs([g_com], max(K // 4, 5), torch)
+    assert rnd.error_bits() == 0, "device error bits set"
+
+    e = 2 if cfg.dtype == "bf16" else 4
+    dominant, bytes_fn = DOMINANT[args.path]
+    vbytes = bytes_fn(f.sizes(), H, cfg.d_k, cfg.d_v, e)
+    cbytes = commit_algorithmic_bytes(f, L, H, cfg.d_k, cfg.d_v, e)
+    ms_layer = ms_verify / L
+    step = ms_round[args.path]
+    achieved = vbytes / (ms_layer * 1e-3) / 1e9
+    c_achieved = cbytes / (ms_commit * 1e-3) / 1e9
+    out = {
+        "metric": "tree nodes x heads verified/sec per GDN layer",
+        "value": N * H * L / (step * 1e-3),
+        "unit": "node-heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one round over L={L} layers, B={B} trees x T={cfg.T} nodes "
+                        f"(random recursive, depth<={cfg.D}), H={H}, d_k=d_v={cfg.d_k}, "
+                        f"{cfg.dtype} q/k/v, f32 gates and state; step = {L} x "
+                        f"{dominant} + one commit over all layers",
+            "L": L, "B": B, "T": cfg.T, "H": H, "d_k": cfg.d_k, "d_v": cfg.d_v, "nodes": N,
+            "path": args.path,
+            "timing": "HIP graph replays of whole rounds; verify and commit also alone",
+            "ms_per_round": ms_round,
+            "verify_ms_per_layer": ms_layer,
+            "commit_ms_per_round": ms_commit,
+            "gc_bytes_per_round": {"tree/fused (on chip)": 0,
+                                   "split: one workspace reused by every layer":
+                                   int(bole.bole_gc_workspace_bytes(B, H))},
+            "transient_bytes_per_round": {"U + logP": L * N * H * (4 * cfg.d_v + 4)},
+        },
+        "roofline": {
+            "kernel": "bole_" + dominant,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": vbytes,
+        },
+        "commit_roofline": {
+            "kernel": "bole_commit_path",
+            "bound": "hbm",
+            "achieved": c_achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": c_achieved / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": cbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, 0, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,7 +538,8 @@ def main():
     dev = torch.device("cuda:0")
     cfg = W.CONFIGS[args.config]
     if cfg.L != 1:
-        cfg = W.Config(**{**cfg.__dict__, "L": 1})
+        round_main(cfg, args, torch, TreeRound, bole, dev)
+        return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -305,3 +305,54 @@ def make_prefix_bulk(cfg: Config, B: int, layer: int = 0, seed: int = 0) -> Pref
     return PrefixBulk(q=to_storage(q, cfg.dtype), k=to_storage(k, cfg.dtype),
                       v=to_storage(v, cfg.dtype), g=g.astype(np.float32),
                       beta=beta.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# device-side generation for large timing runs
+#
+# The multi-layer round moves gigabytes of token operands and states; drawing
+# them with numpy would dominate the run.  These draw the same distributions
+# (the recipe in the module docstring) with a seeded torch generator on the
+# device.  They serve timing only: the oracle-checked tests use the numpy
+# streams above.
+
+@dataclass
+class DeviceLayer:
+    q: "object"      # [N, H, d_k] token dtype
+    k: "object"
+    v: "object"      # [N, H, d_v]
+    g: "object"      # [N, H] float32
+    beta: "object"   # [N, H] float32
+
+
+def _device_gen(torch, dev, cfg: Config, stream: int, *parts: int):
+    seq = np.random.SeedSequence([cfg.cid, stream, *parts])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seq.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1)))
+    return gen
+
+
+def device_layer(cfg: Config, N: int, layer: int, seed: int, torch, dev, lead=()) -> DeviceLayer:
+    """One layer's token operands (or a [*lead, N, H, ...] batch of them)."""
+    gen = _device_gen(torch, dev, cfg, STREAM_TOKENS, seed, layer, 1 << 21)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    H = cfg.H
+
+    def unit(d):
+        x = torch.randn(*lead, N, H, d, generator=gen, device=dev, dtype=torch.float32)
+        return (x / x.norm(dim=-1, keepdim=True)).to(tdt)
+
+    q, k = unit(cfg.d_k), unit(cfg.d_k)
+    v = torch.randn(*lead, N, H, cfg.d_v, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    x = torch.randn(*lead, N, H, generator=gen, device=dev, dtype=torch.float64) + cfg.gate_mu
+    g = (-torch.nn.functional.softplus(x)).to(torch.float32)
+    beta = torch.sigmoid(torch.randn(*lead, N, H, generator=gen, device=dev,
+                                      dtype=torch.float64)).to(torch.float32)
+    return DeviceLayer(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=g.contiguous(),
+                       beta=beta.contiguous())
+
+
+def device_prefix(cfg: Config, B: int, layer: int, seed: int, torch, dev) -> DeviceLayer:
+    """The committed-prefix tokens of all B x H state heads of one layer,
+    [P, B, H, ...] (P = cfg.prefix)."""
+    return device_layer(cfg, B, layer, seed + (1 << 20), torch, dev, lead=(cfg.prefix,))
