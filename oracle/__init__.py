@@ -16,8 +16,10 @@ Two independent formulations live here:
   the finite Neumann series of Lemma 3, plus Eq. 10 for the commit.  It is used
   as a pin for the walk (the two must agree to rounding) and as the reference
   for the G/C factors.
+* ``tree_conv`` (numpy): the tree-parallel short causal convolution of the
+  pipeline's first stage and its conv-state commit, one node at a time.
 
-Pins of the oracle itself are in tests/test_oracle.py.
+Pins of the oracle itself are in tests/test_oracle.py and tests/test_oracle_conv.py.
 """
 
 from __future__ import annotations
@@ -30,6 +32,7 @@ from typing import Optional
 import numpy as np
 
 from .closed_form import closed_form_tree, commit_closed_form, tree_factors  # noqa: F401
+from .tree_conv import conv_commit, tree_conv  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bole_oracle.c")
