@@ -346,6 +346,38 @@ def cpu_baseline(cfg, seed, budget_s=12.0):
                       f"{f.N} nodes x {cfg.H} heads, float64) in {el:.1f} s"}
 
 
+def conv_algorithmic_bytes(N, B, C, Wd, e):
+    """bole_tree_conv: inputs read and outputs written once, each request's
+    committed conv state and the weights read once."""
+    return N * C * e * 2 + B * (Wd - 1) * C * e + C * (Wd + 1) * 4
+
+
+def time_tree_conv(cfg, sets, torch, bole, dev, reps):
+    """The first-stage tree convolution at the workload's shape: C = H (2 d_k +
+    d_v) channels (the mixed q, k, v projection), width W.CONV_WIDTH.  Returns
+    (ms per launch, algorithmic bytes per launch)."""
+    C, Wd = W.conv_channels(cfg), W.CONV_WIDTH
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    runs = []
+    for s_ in sets:
+        t = s_.rnd.topo
+        N, B = s_.forest.N, s_.forest.B
+        x = torch.randn(N, C, generator=gen, device=dev).to(tdt)
+        st = torch.randn(B, Wd - 1, C, generator=gen, device=dev).to(tdt)
+        wgt = torch.randn(C, Wd, generator=gen, device=dev) / Wd ** 0.5
+        bias = 0.1 * torch.randn(C, generator=gen, device=dev)
+        runs.append((x, wgt, bias, st, s_.slot, t.parent, t.tree_off, torch.empty_like(x),
+                     s_.rnd.err))
+    n_in = 4 * len(sets)
+    g = capture(torch, lambda: [bole.bole_tree_conv(*runs[i % len(runs)]) for i in range(n_in)])
+    ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
+    e = 2 if cfg.dtype == "bf16" else 4
+    nbytes = np.mean([conv_algorithmic_bytes(s_.forest.N, s_.forest.B, C, Wd, e) for s_ in sets])
+    return ms, nbytes
+
+
 def commit_algorithmic_bytes(forest, L, H, d_k, d_v, e):
     """Compulsory HBM bytes of one commit over L layers: every committed slot
     read and written once (float32), plus the accepted path's key and U rows."""
@@ -601,6 +633,7 @@ def main():
         g = capture(torch, lambda w_=which: [launch(sets[i % len(sets)], bole, w_)
                                               for i in range(n_in)])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
+    conv_ms, conv_bytes = time_tree_conv(cfg, sets, torch, bole, dev, K)
     for s_ in sets:
         assert s_.rnd.error_bits() == 0, "device error bits set"
     dominant, bytes_fn = DOMINANT[args.path]
@@ -635,6 +668,14 @@ def main():
             "ms_per_step_other_path": ms_other,
             "ms_per_step_eager_launches": ms_eager,
             "kernel_ms_back_to_back": avg,
+            "stage1_tree_conv": {
+                "note": "first pipeline stage (short causal conv + bias + SiLU along parent "
+                        "links), not part of the step",
+                "channels": W.conv_channels(cfg), "width": W.CONV_WIDTH, "ms": conv_ms,
+                "achieved_GBs": conv_bytes / (conv_ms * 1e-3) / 1e9,
+                "frac_of_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "algorithmic_bytes_per_launch": conv_bytes,
+            },
         },
         "roofline": {
             "kernel": "bole_" + dominant,

@@ -208,6 +208,49 @@ BOLE_API int bole_tree_verify(int32_t dtype, const void* q, const void* k, const
                               uint32_t* err, void* stream);
 
 /*
+ * bole_tree_conv - tree-parallel short causal convolution, the first per-layer
+ * stage of the fused tree pipeline (arXiv page, sections II-A and IV-C; review
+ * page, fused-pipeline paragraph: each node fuses convolution, bias and SiLU
+ * along its parent links, all nodes at once).
+ *
+ * Node i's window is the last W entries of its request's committed conv state
+ * (the W - 1 inputs that preceded the tree, oldest first) followed by the
+ * inputs along i's root-to-node path; every root of a tree starts from that
+ * state.  Per channel c:
+ *     y[i][c] = silu(bias[c] + sum_{j<W} weight[c][j] * window_i[j][c]),
+ * tap W-1 multiplying node i's own input.  float32 arithmetic.
+ *
+ *  in   x[N,C]                         dtype, the node inputs (channels contiguous)
+ *  in   weight[C,W], bias[C] or NULL   float32
+ *  in   conv_state[n_slots,W-1,C]      dtype, oldest row first (unused when W == 1)
+ *  in   slot[B], parent[N], tree_off[B+1]
+ *  out  y[N,C]                         dtype; must not alias x
+ *  out  err                            BAD_PARENT, CYCLE, TREE_SIZE, BAD_SLOT
+ * Requires 1 <= W <= 8, C a multiple of 8 and x, y, conv_state 16-byte aligned
+ * (BOLE_E_UNSUPPORTED otherwise).  A rejected tree gets no outputs.
+ */
+BOLE_API int bole_tree_conv(int32_t dtype, const void* x, const float* weight, const float* bias,
+                            const void* conv_state, int32_t n_slots, const int32_t* slot,
+                            const int32_t* parent, const int32_t* tree_off, int32_t B, int32_t N,
+                            int32_t C, int32_t W, void* y, uint32_t* err, void* stream);
+
+/*
+ * bole_conv_commit - the accepted path's conv state, in place: slot[b]'s state
+ * becomes the last W - 1 entries of itself followed by the inputs along the
+ * path root..accept[b]; accept[b] == -1 leaves it bit-unchanged.  (The
+ * counterpart of bole_commit_path for the convolution's short state.)
+ *
+ *  in/out conv_state[n_slots,W-1,C]  dtype
+ *  in     slot[B], x[N,C] (the round's conv inputs), parent[N], tree_off[B+1], accept[B]
+ *  out    err                        BAD_PARENT, CYCLE, TREE_SIZE, BAD_ACCEPT, BAD_SLOT
+ * With W == 1 there is no state (conv_state may be NULL) and nothing is launched.
+ */
+BOLE_API int bole_conv_commit(int32_t dtype, void* conv_state, int32_t n_slots,
+                              const int32_t* slot, const void* x, const int32_t* parent,
+                              const int32_t* tree_off, const int32_t* accept, int32_t B, int32_t N,
+                              int32_t C, int32_t W, uint32_t* err, void* stream);
+
+/*
  * bole_commit_path - accepted-path state reconstruction for L layers in one
  * launch, in place (paper Eq. 10; review: unified cross-layer state commit).
  *

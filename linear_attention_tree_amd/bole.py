@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.bole_tree_verify.restype = ctypes.c_int
         L.bole_tree_verify.argtypes = ([i32, P, P, P, P, P, P, P, i32, P, P]
                                        + [i32] * 5 + [P] * 9)
+        L.bole_tree_conv.restype = ctypes.c_int
+        L.bole_tree_conv.argtypes = [i32, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, P, P, P]
+        L.bole_conv_commit.restype = ctypes.c_int
+        L.bole_conv_commit.argtypes = [i32, P, i32, P, P, P, P, P, i32, i32, i32, i32, P, P]
         L.bole_commit_path.restype = ctypes.c_int
         L.bole_commit_path.argtypes = [i32, P, i64, i32, P, i32, P, i64, P, i64, P, i64, P, P,
                                        P, i32, i32, i32, i32, i32, P, P]
@@ -303,6 +307,59 @@ def bole_tree_verify(q, k, v, parent, log_gamma, beta, state_pool, slot, tree_of
         _ptr(state_pool), state_pool.shape[0], _ptr(slot), _ptr(tree_off), B, N, H, d_k, d_v,
         _ptr(O), _ptr(U), _ptr(depth), _ptr(anc), _ptr(order), _ptr(tree_depth), _ptr(logP),
         _ptr(err), _stream(stream)))
+
+
+def bole_tree_conv(x, weight, bias, conv_state, slot, parent, tree_off, y, err=None,
+                   stream=None):
+    """Tree-parallel short causal convolution (+ bias, SiLU) of x [N, C]."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    N, C = x.shape
+    _need(weight, "weight", torch.float32, 2)
+    W = weight.shape[1]
+    if weight.shape[0] != C:
+        raise ValueError("weight must be [C, W]")
+    _need(bias, "bias", torch.float32, 1, allow_none=True)
+    if bias is not None and bias.shape[0] != C:
+        raise ValueError("bias must be [C]")
+    _need(parent, "parent", torch.int32, 1)
+    _need(tree_off, "tree_off", torch.int32, 1)
+    B = tree_off.shape[0] - 1
+    n_slots = 0
+    if W > 1:
+        _need(conv_state, "conv_state", x.dtype, 3)
+        _need(slot, "slot", torch.int32, 1)
+        if tuple(conv_state.shape[1:]) != (W - 1, C):
+            raise ValueError("conv_state must be [n_slots, W-1, C]")
+        if slot.shape[0] != B:
+            raise ValueError("slot needs B entries")
+        n_slots = conv_state.shape[0]
+    _need(y, "y", x.dtype, 2)
+    if tuple(y.shape) != (N, C) or parent.shape[0] != N:
+        raise ValueError("y must be [N, C] and parent [N]")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_tree_conv", lib().bole_tree_conv(
+        _code(x.dtype), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state if W > 1 else None),
+        n_slots, _ptr(slot if W > 1 else None), _ptr(parent), _ptr(tree_off), B, N, C, W, _ptr(y),
+        _ptr(err), _stream(stream)))
+
+
+def bole_conv_commit(conv_state, slot, x, parent, tree_off, accept, err=None, stream=None):
+    """The accepted paths' conv states, in place."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    N, C = x.shape
+    _need(conv_state, "conv_state", x.dtype, 3)
+    W = conv_state.shape[1] + 1
+    if conv_state.shape[2] != C:
+        raise ValueError("conv_state must be [n_slots, W-1, C]")
+    for t, nm in ((slot, "slot"), (parent, "parent"), (tree_off, "tree_off"), (accept, "accept")):
+        _need(t, nm, torch.int32, 1)
+    B = tree_off.shape[0] - 1
+    if slot.shape[0] != B or accept.shape[0] != B or parent.shape[0] != N:
+        raise ValueError("slot and accept need B entries, parent N")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_conv_commit", lib().bole_conv_commit(
+        _code(x.dtype), _ptr(conv_state), conv_state.shape[0], _ptr(slot), _ptr(x), _ptr(parent),
+        _ptr(tree_off), _ptr(accept), B, N, C, W, _ptr(err), _stream(stream)))
 
 
 def _layer_view(t, name, inner_ndim):

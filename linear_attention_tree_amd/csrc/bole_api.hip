@@ -28,6 +28,12 @@ int bole_tree_verify_launch(int32_t, const void*, const void*, const void*, cons
                             const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
                             float*, int32_t*, uint64_t*, int32_t*, int32_t*, float*, uint32_t*,
                             hipStream_t);
+int bole_tree_conv_launch(int32_t, const void*, const float*, const float*, const void*, int32_t,
+                          const int32_t*, const int32_t*, const int32_t*, int32_t, int32_t, int32_t,
+                          int32_t, void*, uint32_t*, hipStream_t);
+int bole_conv_commit_launch(int32_t, void*, int32_t, const int32_t*, const void*, const int32_t*,
+                            const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
+                            uint32_t*, hipStream_t);
 int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
@@ -39,6 +45,10 @@ namespace {
 constexpr int32_t kMaxGrid = 1 << 30;
 
 bool head_dim_ok(int32_t d) { return d >= 16 && d <= 256 && d % 16 == 0; }
+
+constexpr int32_t kMaxConvWidth = 8;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool dtype_ok(int32_t dt) { return dt == BOLE_F32 || dt == BOLE_BF16; }
 
@@ -134,6 +144,34 @@ int bole_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
   return bole_tree_verify_launch(dtype, q, k, v, parent, log_gamma, beta, state_pool, n_slots,
                                  slot, tree_off, B, N, H, d_k, d_v, O, U, depth, anc, order,
                                  tree_depth, logP, err, (hipStream_t)stream);
+}
+
+int bole_tree_conv(int32_t dtype, const void* x, const float* weight, const float* bias,
+                   const void* conv_state, int32_t n_slots, const int32_t* slot,
+                   const int32_t* parent, const int32_t* tree_off, int32_t B, int32_t N, int32_t C,
+                   int32_t W, void* y, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!x || !weight || !parent || !tree_off || !y || (W > 1 && (!conv_state || !slot)))
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || C < 1 || B > (1 << 24) || (W > 1 && n_slots < 1)) return BOLE_E_SHAPE;
+  if (W < 1 || W > kMaxConvWidth || C % 8 != 0 || C > (1 << 24) || !aligned16(x) ||
+      !aligned16(y) || (W > 1 && !aligned16(conv_state)))
+    return BOLE_E_UNSUPPORTED;
+  return bole_tree_conv_launch(dtype, x, weight, bias, conv_state, n_slots, slot, parent,
+                               tree_off, B, N, C, W, y, err, (hipStream_t)stream);
+}
+
+int bole_conv_commit(int32_t dtype, void* conv_state, int32_t n_slots, const int32_t* slot,
+                     const void* x, const int32_t* parent, const int32_t* tree_off,
+                     const int32_t* accept, int32_t B, int32_t N, int32_t C, int32_t W,
+                     uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if ((W > 1 && !conv_state) || !slot || !x || !parent || !tree_off || !accept) return BOLE_E_NULL;
+  if (B < 1 || N < 1 || C < 1 || n_slots < 1 || B > (1 << 24)) return BOLE_E_SHAPE;
+  if (W < 1 || W > kMaxConvWidth || C > (1 << 24)) return BOLE_E_UNSUPPORTED;
+  if (W == 1) return BOLE_OK;  // no state to move
+  return bole_conv_commit_launch(dtype, conv_state, n_slots, slot, x, parent, tree_off, accept, B,
+                                 N, C, W, err, (hipStream_t)stream);
 }
 
 int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,

@@ -1,0 +1,297 @@
+// Tree-parallel short causal convolution: the first per-layer stage of the
+// fused tree pipeline (arXiv page of Bole, section IV-C; review page, fused
+// pipeline paragraph: every node fuses convolution, bias and SiLU along its
+// parent links, all nodes at once).  The GDN layer's depthwise causal
+// convolution (arXiv page, section II-A) sees, at node i, the last W entries of
+// the request's committed conv state (the W - 1 inputs that preceded the tree,
+// oldest first) followed by the inputs along i's root-to-node path: exactly
+// what ordinary decoding of that path would see.
+//
+// y[i][c] = silu(bias[c] + sum_j weight[c][j] * window_i[j][c]), tap W-1 on
+// node i's own input.  float32 arithmetic (SiLU on the hardware exp2 and
+// reciprocal), output in the token dtype.
+//
+// The commit moves the accepted path's last W - 1 inputs into the request's
+// conv state, in place.
+#include <type_traits>
+
+#include "tree_topo.h"
+
+namespace bole {
+
+constexpr int kMaxConv = 8;        // widest convolution supported
+constexpr int kConvThreads = 256;
+
+template <int DT>
+struct ConvCfg {
+  using Elem = std::conditional_t<DT == BOLE_BF16, uint16_t, float>;
+  static constexpr int EPP = 16 / sizeof(Elem);              // elements per 16-byte piece
+  static constexpr int CH = DT == BOLE_BF16 ? 256 : 128;      // channels per workgroup (512 B)
+  static constexpr int GROUPS = CH / EPP;                    // pieces per row
+  static constexpr int NODE_LANES = kConvThreads / GROUPS;   // nodes computed at once
+};
+
+__device__ __forceinline__ float elem_to_float(uint16_t b) { return bf16_bits_to_float(b); }
+__device__ __forceinline__ float elem_to_float(float f) { return f; }
+
+// grid (B, ceil(C / CH)).  Rows 0..T-1 of the LDS tile hold the tree's inputs
+// for the workgroup's channels, rows kMaxTree .. kMaxTree + W - 2 the committed
+// conv state.  src[i][j] is the tile row of the j-th most recent entry of node
+// i's window (j = 0: node i itself).
+template <int DT>
+__global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
+    const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
+    const void* __restrict__ conv_state, int32_t n_slots, const int32_t* __restrict__ slot,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ tree_off, int32_t N, int32_t C,
+    int32_t Wd, void* __restrict__ y, uint32_t* __restrict__ err) {
+  using CC = ConvCfg<DT>;
+  using Elem = typename CC::Elem;
+  __shared__ __align__(16) Elem tile[kMaxTree + kMaxConv - 1][CC::CH];
+  __shared__ float ws[kMaxConv][CC::CH];
+  __shared__ float bs[CC::CH];
+  __shared__ int8_t src[kMaxTree][kMaxConv];
+  __shared__ int tree_ok;
+
+  const int b = blockIdx.x;
+  const int c0 = CC::CH * blockIdx.y;
+  const bool reporter = threadIdx.x == 0 && blockIdx.y == 0;
+  const int off = tree_off[b], end = tree_off[b + 1];
+  const int T = end - off;
+  if (off < 0 || end > N || T < 1 || T > kMaxTree) {
+    if (reporter) report(err, BOLE_ERR_TREE_SIZE);
+    return;
+  }
+  const int s = Wd > 1 ? slot[b] : 0;
+  if (Wd > 1 && (s < 0 || s >= n_slots)) {
+    if (reporter) report(err, BOLE_ERR_BAD_SLOT);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const Elem* xe = reinterpret_cast<const Elem*>(x);
+  const Elem* se = reinterpret_cast<const Elem*>(conv_state);
+
+  // Every load goes out before any is waited on: wave 0's parent links first
+  // (the topology below waits only for them), then each thread's pieces of
+  // the tree's input rows and the committed state rows, then the weights.  A
+  // piece past the rows needed or past C reads piece 0 of row 0 and is not
+  // stored.
+  int p = -1;
+  if (w == 0) p = parent[off + min(lane, T - 1)];
+  constexpr int kPieces = (kMaxTree + kMaxConv - 1) * CC::GROUPS / kConvThreads + 1;
+  const int n_pieces = (T + Wd - 1) * CC::GROUPS;
+  u16x8 buf[kPieces];
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int id = threadIdx.x + kConvThreads * k;
+    const int r = id / CC::GROUPS, pc = id - (id / CC::GROUPS) * CC::GROUPS;
+    const int c = c0 + CC::EPP * pc;
+    const bool use = id < n_pieces && c < C;
+    const Elem* row = !use ? xe : r < T ? xe + (int64_t)(off + r) * C
+                                        : se + ((int64_t)s * (Wd - 1) + (r - T)) * C;
+    buf[k] = *reinterpret_cast<const u16x8*>(row + (use ? c : 0));
+  }
+  constexpr int kWPer = kMaxConv * CC::CH / kConvThreads;
+  float wv[kWPer];
+#pragma unroll
+  for (int k = 0; k < kWPer; ++k) {
+    const int id = threadIdx.x + kConvThreads * k;
+    const int j = id / CC::CH, c = id - (id / CC::CH) * CC::CH;
+    const bool use = j < Wd && c0 + c < C;
+    wv[k] = weight[use ? (int64_t)(c0 + c) * Wd + j : 0];
+  }
+  const int cb = min(c0 + (int)threadIdx.x, C - 1);
+  const float bv = bias != nullptr ? bias[cb] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (w == 0) {
+    const TreeTopo tp = tree_topology(lane, T, p);
+    if (!tp.fail && lane < T) {
+      // walk up: entry j is the j-th ancestor while the path lasts, then the
+      // committed state from its newest row backwards (the shuffles read
+      // parents of tree nodes, all active lanes)
+      int cur = lane;
+      for (int j = 0; j < Wd; ++j) {
+        src[lane][j] = (int8_t)(j <= tp.dep ? cur : kMaxTree + (Wd - 1) - (j - tp.dep));
+        const int up = __shfl(p, max(cur, 0));
+        cur = j < tp.dep ? up : -1;
+      }
+    }
+    if (lane == 0) {
+      tree_ok = !tp.fail;
+      if (tp.fail && reporter) report(err, tp.fail);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int id = threadIdx.x + kConvThreads * k;
+    const int r = id / CC::GROUPS, pc = id - (id / CC::GROUPS) * CC::GROUPS;
+    if (id < n_pieces && c0 + CC::EPP * pc < C)
+      *reinterpret_cast<u16x8*>(&tile[r < T ? r : kMaxTree + r - T][CC::EPP * pc]) = buf[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kWPer; ++k) {
+    const int id = threadIdx.x + kConvThreads * k;
+    ws[id / CC::CH][id - (id / CC::CH) * CC::CH] = wv[k];
+  }
+  if (threadIdx.x < CC::CH) bs[threadIdx.x] = c0 + (int)threadIdx.x < C ? bv : 0.0f;
+  __syncthreads();
+  if (!tree_ok) return;
+
+  const int pc = threadIdx.x % CC::GROUPS, nl = threadIdx.x / CC::GROUPS;
+  const int cl = CC::EPP * pc, c = c0 + cl;
+  if (c >= C) return;  // no barrier follows
+  Elem* ye = reinterpret_cast<Elem*>(y) + c;
+  auto nodes = [&](auto wd_tag) {
+    constexpr int WD = decltype(wd_tag)::value;
+    // the thread's taps and bias stay in registers across its nodes
+    float wr[WD][CC::EPP], br[CC::EPP];
+#pragma unroll
+    for (int e = 0; e < CC::EPP; ++e) {
+      br[e] = bs[cl + e];
+#pragma unroll
+      for (int j = 0; j < WD; ++j) wr[j][e] = ws[j][cl + e];
+    }
+    for (int i = nl; i < T; i += CC::NODE_LANES) {
+      float acc[CC::EPP];
+#pragma unroll
+      for (int e = 0; e < CC::EPP; ++e) acc[e] = br[e];
+#pragma unroll
+      for (int j = 0; j < WD; ++j) {  // j-th most recent entry, tap WD-1-j
+        const u16x8 raw = *reinterpret_cast<const u16x8*>(&tile[src[i][j]][cl]);
+        const Elem* v = reinterpret_cast<const Elem*>(&raw);
+#pragma unroll
+        for (int e = 0; e < CC::EPP; ++e) acc[e] = fmaf(wr[WD - 1 - j][e], elem_to_float(v[e]), acc[e]);
+      }
+      u16x8 out;
+      Elem* o = reinterpret_cast<Elem*>(&out);
+#pragma unroll
+      for (int e = 0; e < CC::EPP; ++e) {
+        // SiLU a / (1 + e^-a) on the hardware exp2 and reciprocal (relative
+        // error near 1e-6 for |a| < 100; e^-a overflows to inf, giving -0, for
+        // very negative a)
+        const float a = acc[e];
+        const float sv = a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
+        if constexpr (DT == BOLE_BF16)
+          o[e] = float_to_bf16_bits(sv);
+        else
+          o[e] = sv;
+      }
+      // streamed out: the outputs are not read again by this kernel
+      __builtin_nontemporal_store(out, reinterpret_cast<u16x8*>(ye + (int64_t)(off + i) * C));
+    }
+  };
+  switch (Wd) {
+    case 1: nodes(std::integral_constant<int, 1>{}); break;
+    case 2: nodes(std::integral_constant<int, 2>{}); break;
+    case 3: nodes(std::integral_constant<int, 3>{}); break;
+    case 4: nodes(std::integral_constant<int, 4>{}); break;
+    case 5: nodes(std::integral_constant<int, 5>{}); break;
+    case 6: nodes(std::integral_constant<int, 6>{}); break;
+    case 7: nodes(std::integral_constant<int, 7>{}); break;
+    default: nodes(std::integral_constant<int, 8>{}); break;
+  }
+}
+
+// grid (B, ceil(C / 256)); thread = channel.  Reads every source of the new
+// state before writing any of it (the update is in place).
+template <int DT>
+__global__ __launch_bounds__(kConvThreads) void conv_commit_kernel(
+    void* __restrict__ conv_state, int32_t n_slots, const int32_t* __restrict__ slot,
+    const void* __restrict__ x, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ tree_off, const int32_t* __restrict__ accept, int32_t N, int32_t C,
+    int32_t Wd, uint32_t* __restrict__ err) {
+  using Elem = typename ConvCfg<DT>::Elem;
+  __shared__ int srcs[kMaxConv];  // >= 0: tree node; < 0: -1 - (old state row)
+  __shared__ int tree_ok;
+  const int b = blockIdx.x;
+  const int a = accept[b];
+  if (a == -1 || Wd < 2) return;
+  const bool reporter = threadIdx.x == 0 && blockIdx.y == 0;
+  const int off = tree_off[b], end = tree_off[b + 1];
+  const int T = end - off;
+  if (off < 0 || end > N || T < 1 || T > kMaxTree) {
+    if (reporter) report(err, BOLE_ERR_TREE_SIZE);
+    return;
+  }
+  if (a < 0 || a >= T) {
+    if (reporter) report(err, BOLE_ERR_BAD_ACCEPT);
+    return;
+  }
+  const int s = slot[b];
+  if (s < 0 || s >= n_slots) {
+    if (reporter) report(err, BOLE_ERR_BAD_SLOT);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w == 0) {
+    const int p = parent[off + min(lane, T - 1)];
+    const TreeTopo tp = tree_topology(lane, T, p);
+    if (!tp.fail) {
+      // new row k (oldest first) is the (W-2-k)-th most recent entry of the
+      // accepted path's window
+      const int da = __shfl(tp.dep, a);
+      int cur = a;
+      for (int j = 0; j < Wd - 1; ++j) {
+        if (lane == 0) srcs[Wd - 2 - j] = j <= da ? cur : -1 - ((Wd - 1) - (j - da));
+        const int up = __shfl(p, max(cur, 0));
+        cur = j < da ? up : -1;
+      }
+    }
+    if (lane == 0) {
+      tree_ok = !tp.fail;
+      if (tp.fail && reporter) report(err, tp.fail);
+    }
+  }
+  __syncthreads();
+  if (!tree_ok) return;
+  const int c = 256 * blockIdx.y + threadIdx.x;
+  if (c >= C) return;
+  Elem* st = reinterpret_cast<Elem*>(conv_state) + (int64_t)s * (Wd - 1) * C + c;
+  const Elem* xe = reinterpret_cast<const Elem*>(x) + c;
+  Elem vals[kMaxConv];
+#pragma unroll
+  for (int k = 0; k < kMaxConv - 1; ++k) {
+    if (k < Wd - 1) {
+      const int sr = srcs[k];
+      vals[k] = sr >= 0 ? xe[(int64_t)(off + sr) * C] : st[(int64_t)(-1 - sr) * C];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxConv - 1; ++k)
+    if (k < Wd - 1) st[(int64_t)k * C] = vals[k];
+}
+
+}  // namespace bole
+
+extern "C" int bole_tree_conv_launch(int32_t dtype, const void* x, const float* weight,
+                                     const float* bias, const void* conv_state, int32_t n_slots,
+                                     const int32_t* slot, const int32_t* parent,
+                                     const int32_t* tree_off, int32_t B, int32_t N, int32_t C,
+                                     int32_t W, void* y, uint32_t* err, hipStream_t s) {
+  const dim3 block(bole::kConvThreads);
+  if (dtype == BOLE_BF16) {
+    const dim3 grid(B, (C + bole::ConvCfg<BOLE_BF16>::CH - 1) / bole::ConvCfg<BOLE_BF16>::CH);
+    hipLaunchKernelGGL(bole::tree_conv_kernel<BOLE_BF16>, grid, block, 0, s, x, weight, bias,
+                       conv_state, n_slots, slot, parent, tree_off, N, C, W, y, err);
+  } else {
+    const dim3 grid(B, (C + bole::ConvCfg<BOLE_F32>::CH - 1) / bole::ConvCfg<BOLE_F32>::CH);
+    hipLaunchKernelGGL(bole::tree_conv_kernel<BOLE_F32>, grid, block, 0, s, x, weight, bias,
+                       conv_state, n_slots, slot, parent, tree_off, N, C, W, y, err);
+  }
+  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
+}
+
+extern "C" int bole_conv_commit_launch(int32_t dtype, void* conv_state, int32_t n_slots,
+                                       const int32_t* slot, const void* x, const int32_t* parent,
+                                       const int32_t* tree_off, const int32_t* accept, int32_t B,
+                                       int32_t N, int32_t C, int32_t W, uint32_t* err,
+                                       hipStream_t s) {
+  const dim3 grid(B, (C + 255) / 256), block(bole::kConvThreads);
+  if (dtype == BOLE_BF16)
+    hipLaunchKernelGGL(bole::conv_commit_kernel<BOLE_BF16>, grid, block, 0, s, conv_state,
+                       n_slots, slot, x, parent, tree_off, accept, N, C, W, err);
+  else
+    hipLaunchKernelGGL(bole::conv_commit_kernel<BOLE_F32>, grid, block, 0, s, conv_state,
+                       n_slots, slot, x, parent, tree_off, accept, N, C, W, err);
+  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
+}

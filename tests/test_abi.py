@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(L):
     names = declared_symbols()
     assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
                           "bole_verify", "bole_factor_verify", "bole_tree_verify",
-                          "bole_commit_path", "bole_status_string"}
+                          "bole_commit_path", "bole_tree_conv", "bole_conv_commit",
+                          "bole_status_string"}
     for n in names:
         assert hasattr(L, n), n
         assert hasattr(lat, n), n   # same names in the Python binding
@@ -42,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_internal_launchers_are_hidden(L):
     for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch",
-              "bole_tree_verify_launch"):
+              "bole_tree_verify_launch", "bole_tree_conv_launch", "bole_conv_commit_launch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
 
@@ -120,6 +121,40 @@ def test_tree_verify_argument_errors(L):
     assert call(dk=256) == E_UNSUPPORTED
     assert call(dtype=0, dk=128) == E_UNSUPPORTED
     assert call(dv=40) == E_UNSUPPORTED
+
+
+def test_tree_conv_argument_errors(L):
+    f = L.bole_tree_conv
+    A = ctypes.c_void_p(0x1000)          # 16-byte aligned, never dereferenced
+    U = ctypes.c_void_p(0x1002)          # not 16-byte aligned
+
+    def call(dtype=1, x=A, st=A, B=1, N=1, C=64, W=4, y=A, slot=A):
+        return f(dtype, x, A, None, st, 1, slot, A, A, B, N, C, W, y, None, None)
+
+    assert call(dtype=4) == E_DTYPE
+    assert call(x=None) == E_NULL
+    assert call(st=None) == E_NULL            # a state is needed for W > 1
+    # no state is needed for W == 1: validation gets past the pointers and stops
+    # at the channel count (nothing is launched)
+    assert call(st=None, slot=None, W=1, C=12) == E_UNSUPPORTED
+    assert call(B=0) == E_SHAPE
+    assert call(W=9) == E_UNSUPPORTED
+    assert call(W=0) == E_UNSUPPORTED
+    assert call(C=12) == E_UNSUPPORTED        # not a multiple of 8
+    assert call(y=U) == E_UNSUPPORTED
+
+
+def test_conv_commit_argument_errors(L):
+    f = L.bole_conv_commit
+
+    def call(dtype=1, st=FAKE, acc=FAKE, B=1, W=4):
+        return f(dtype, st, 1, FAKE, FAKE, FAKE, FAKE, acc, B, 1, 64, W, None, None)
+
+    assert call(dtype=2) == E_DTYPE
+    assert call(st=None) == E_NULL
+    assert call(acc=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(W=9) == E_UNSUPPORTED
 
 
 def test_commit_argument_errors(L):

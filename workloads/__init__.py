@@ -356,3 +356,48 @@ def device_prefix(cfg: Config, B: int, layer: int, seed: int, torch, dev) -> Dev
     """The committed-prefix tokens of all B x H state heads of one layer,
     [P, B, H, ...] (P = cfg.prefix)."""
     return device_layer(cfg, B, layer, seed + (1 << 20), torch, dev, lead=(cfg.prefix,))
+
+
+# ----------------------------------------------------------------------------
+# short causal convolution inputs
+
+STREAM_CONV = 4
+CONV_WIDTH = 4  # GDN's usual kernel width; the pages do not fix one
+
+
+@dataclass
+class ConvInputs:
+    """Inputs of the tree convolution for one layer: x [N, C] and the committed
+    conv states [n_slots, W-1, C] (storage arrays, as for LayerInputs), float32
+    weights [C, W] and bias [C]."""
+    x: np.ndarray
+    weight: np.ndarray
+    bias: np.ndarray
+    state: np.ndarray
+    dtype: str
+
+    @property
+    def x64(self):
+        return widen(self.x, self.dtype)
+
+    @property
+    def state64(self):
+        return widen(self.state, self.dtype)
+
+
+def conv_channels(cfg: Config) -> int:
+    """The mixed q, k, v projection a GDN layer convolves: 2 H d_k + H d_v."""
+    return cfg.H * (2 * cfg.d_k + cfg.d_v)
+
+
+def make_conv(cfg: Config, N: int, n_slots: int, C: Optional[int] = None, W: int = CONV_WIDTH,
+              layer: int = 0, seed: int = 0) -> ConvInputs:
+    """x, states ~ N(0, 1); weight ~ N(0, 1/W); bias ~ N(0, 0.01)."""
+    rng = _rng(seed, cfg, STREAM_CONV, layer, W)
+    C = conv_channels(cfg) if C is None else C
+    x = rng.standard_normal((N, C), dtype=np.float32)
+    st = rng.standard_normal((n_slots, W - 1, C), dtype=np.float32)
+    w = (rng.standard_normal((C, W)) / np.sqrt(W)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return ConvInputs(x=to_storage(x, cfg.dtype), weight=w, bias=b,
+                      state=to_storage(st, cfg.dtype), dtype=cfg.dtype)
