@@ -31,7 +31,8 @@ from typing import Optional
 
 import numpy as np
 
-from .closed_form import closed_form_tree, commit_closed_form, tree_factors  # noqa: F401
+from .closed_form import (closed_form_tree, commit_closed_form, inverse_factors,  # noqa: F401
+                          tree_factors)
 from .tree_conv import conv_commit, tree_conv  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -13,6 +13,8 @@ section 三, Eqs. 2, 4, 5, 6, 10), for one tree and one head:
   B0        = D_P Q S_pre                                            (Eq. 2 / Eq. 7)
   U         = (I + G)^{-1} R = sum_{m=0}^{d} (-G)^m R                (Eq. 5, Eq. 6)
   O         = B0 + C U                                               (Eq. 2)
+  W         = (I + G)^{-1} = sum_{m=0}^{d} (-G)^m, M = C W            (Lemma 3; an explicit
+                                                                      inverse, one exact solve)
   S_new     = P_a S_pre + (D_a K_a)^T U_a  for the path a            (Eq. 10)
 
 Here S_pre is the paper's d_k x d_v state.  The serving slot stores its
@@ -76,6 +78,19 @@ def closed_form_tree(parent, q, k, v, g, beta, S_slot):
         U = U + Z
     O = B0 + C @ U
     return dict(O=O, U=U, G=G, C=C, R=R, B0=B0, P=P, d=d)
+
+
+def inverse_factors(G, C, d):
+    """W = (I + G)^{-1} as the finite Neumann polynomial sum_{m=0}^{d} (-G)^m
+    (Lemma 3: G^{d+1} = 0), and M = C W, so that U = W R and O = B0 + M R."""
+    G = np.asarray(G, dtype=np.float64)
+    T = G.shape[0]
+    W = np.eye(T)
+    term = np.eye(T)
+    for _ in range(d):
+        term = -G @ term
+        W = W + term
+    return W, np.asarray(C, dtype=np.float64) @ W
 
 
 def commit_closed_form(parent, a, k, U, P, S_slot):

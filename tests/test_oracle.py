@@ -13,7 +13,7 @@ import pytest
 import scipy.linalg
 
 import oracle
-from oracle.closed_form import closed_form_tree, commit_closed_form, tree_factors
+from oracle.closed_form import closed_form_tree, commit_closed_form, inverse_factors, tree_factors
 import workloads as W
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -175,7 +175,7 @@ def test_nilpotency_depth_bound():
 
 
 def test_unit_determinant():
-    """Check 4 (L33 of the arXiv text: I+G is unit lower triangular, det = 1):
+    """Check 4 (arXiv page, Theorem 1 discussion: I+G is unit lower triangular, det = 1):
     in level order the strict upper part is exactly 0 and the diagonal exactly 1."""
     rng = np.random.default_rng(5)
     for _ in range(50):
@@ -188,6 +188,51 @@ def test_unit_determinant():
         assert np.all(np.triu(M, 1) == 0.0)
         assert np.all(np.diag(M) == 1.0)
         assert abs(np.linalg.det(M) - 1.0) < 1e-12
+
+
+def test_inverse_factors_against_library_inverse():
+    """The explicit-inverse factors: W from the finite Neumann polynomial equals
+    scipy's unit-lower-triangular solve of (I + G) W = I in level order (a
+    library routine), W (I + G) = I, and W R, B0 + M R reproduce U and O of
+    the walk (Lemma 3 and Eq. 2 with the inverse formed first)."""
+    rng = np.random.default_rng(12)
+    for _ in range(60):
+        T = int(rng.integers(1, 33))
+        parent = W.random_tree(rng, T, int(rng.integers(1, 16)))
+        q, k, v, g, beta, S = rand_inputs(rng, T, 8, 5, gate_mu=float(rng.normal()))
+        cf = closed_form_tree(parent, q, k, v, g, beta, S)
+        Wm, M = inverse_factors(cf["G"], cf["C"], cf["d"])
+        order = oracle.tree_prep(parent, np.array([0, T], np.int32))["order"]
+        lev = np.ix_(order, order)
+        Wl = scipy.linalg.solve_triangular(np.eye(T) + cf["G"][lev], np.eye(T), lower=True,
+                                           unit_diagonal=True)
+        assert rel(Wm[lev], Wl) < 1e-12
+        assert rel(Wm @ (np.eye(T) + cf["G"]), np.eye(T)) < 1e-12
+        O, U, _ = walk_one(parent, q, k, v, g, beta, S)
+        assert rel(Wm @ cf["R"], U) < 1e-12
+        assert rel(cf["B0"] + M @ cf["R"], O) < 1e-12
+
+
+def test_inverse_factors_catch_a_short_polynomial():
+    """One Neumann term short (sum to d - 1) misses W on a chain of depth d.
+    Nearly parallel keys, beta near 1 and gates near 1 make every G entry of
+    order 1, so the dropped term (-G)^d is of order 1 too."""
+    rng = np.random.default_rng(13)
+    T = 9
+    parent = np.arange(-1, T - 1, dtype=np.int32)
+    q, k, v, g, beta, S = rand_inputs(rng, T, 8, 5)
+    k = np.ones((T, 8)) + 0.1 * rng.standard_normal((T, 8))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    g = np.full(T, -0.01)
+    beta = np.full(T, 0.9)
+    cf = closed_form_tree(parent, q, k, v, g, beta, S)
+    assert cf["d"] == T - 1
+    W_full, _ = inverse_factors(cf["G"], cf["C"], cf["d"])
+    W_short, _ = inverse_factors(cf["G"], cf["C"], cf["d"] - 1)
+    ref = scipy.linalg.solve_triangular(np.eye(T) + cf["G"], np.eye(T), lower=True,
+                                        unit_diagonal=True)
+    assert rel(W_full, ref) < 1e-12
+    assert rel(W_short, ref) > 1e-3
 
 
 def test_reconstructed_state_every_node():
