@@ -59,6 +59,8 @@ DOMINANT = {  # path -> (launch name, algorithmic bytes of one launch)
     "tree": ("tree_verify", tree_verify_algorithmic_bytes),
     "fused": ("factor_verify", verify_algorithmic_bytes),
     "split": ("verify", verify_algorithmic_bytes),
+    "split_neumann": ("verify_neumann", verify_algorithmic_bytes),
+    "split_inverse": ("verify_inverse", verify_algorithmic_bytes),
 }
 
 
@@ -226,6 +228,15 @@ def launch(s, bole, which):
     elif which == "verify":
         bole.bole_verify(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C, t.order,
                          t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
+    elif which == "verify_neumann":
+        bole.bole_verify_neumann(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C,
+                                 t.order, t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
+    elif which == "factor_inverse":
+        bole.bole_factor_inverse(s.q, s.k, lp, s.beta, t.anc, t.order, t.tree_off, s.rnd.G,
+                                 s.rnd.C, s.rnd.err)
+    elif which == "verify_inverse":
+        bole.bole_verify_inverse(s.q, s.k, s.v, lp, s.beta, s.pool, s.slot, s.rnd.G, s.rnd.C,
+                                 t.order, t.depth, t.tree_off, t.tree_depth, s.O, s.U, s.rnd.err)
     elif which == "tree_verify":
         bole.bole_tree_verify(s.q, s.k, s.v, t.parent, s.g[0], s.beta, s.pool, s.slot, t.tree_off,
                               s.O, s.U, t.depth, t.anc, t.order, t.tree_depth, lp, s.rnd.err)
@@ -246,6 +257,10 @@ STEPS = {
     "fused": ("tree_prep", "factor_verify", "commit"),
     # the four-call path: G/C written by the producer, read back by verify
     "split": ("tree_prep", "factor_gc", "verify", "commit"),
+    # the four-call path with the other exact solves of (I + G) U = R: the
+    # d-step Neumann propagation, and the explicit inverse W = (I+G)^-1, M = C W
+    "split_neumann": ("tree_prep", "factor_gc", "verify_neumann", "commit"),
+    "split_inverse": ("tree_prep", "factor_inverse", "verify_inverse", "commit"),
 }
 
 
@@ -421,7 +436,7 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
     """One step = one verification round over cfg.L layers: the per-layer
     verify launches, then one commit over all layers (in place, so each round
     verifies against the states the previous round committed)."""
-    if args.path == "split":
+    if args.path.startswith("split"):
         raise SystemExit("the multi-layer round runs --path tree or --path fused")
     L, H = cfg.L, cfg.H
     f = W.make_forest(cfg, 0)
@@ -543,7 +558,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotated independent input sets")
     ap.add_argument("--path", default="tree", choices=sorted(STEPS),
                     help="tree: tree_verify + commit; fused: prep + factor_verify + commit; "
-                         "split: the four calls")
+                         "split: the four calls; split_neumann, split_inverse: the four calls "
+                         "with the other exact solves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
@@ -626,7 +642,8 @@ def main():
     ms_eager = time_steps_eager(sets, bole, args.path, max(K // 2, 10), torch)
     # per-kernel averages: each kernel alone, 4 x len(sets) launches per graph
     # over the rotated sets (same inputs, same stream)
-    kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "tree_verify", "commit")
+    kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "tree_verify", "commit",
+               "verify_neumann", "factor_inverse", "verify_inverse")
     avg = {}
     for which in kernels:
         n_in = 4 * len(sets)

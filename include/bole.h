@@ -159,6 +159,63 @@ BOLE_API int bole_verify(int32_t dtype, const void* q, const void* k, const void
                 void* stream);
 
 /*
+ * bole_verify_neumann - bole_verify with (I + G)^-1 R evaluated as the d-step
+ * Neumann propagation the pages run on chip (review Eq. 8 and Lemma 3; arXiv
+ * page section IV-B): Z = U = R, then d_b times Z <- -G Z, U += Z, with d_b =
+ * the tree's depth (the deepest row of depth[]).  The result equals
+ * bole_verify's up to rounding; the two are alternative exact solves of the
+ * same structured system.  Row tiles of Z that are structurally zero at a step
+ * (all rows shallower than the step) are skipped.
+ *
+ *  arguments, outputs and errors as bole_verify.
+ */
+BOLE_API int bole_verify_neumann(int32_t dtype, const void* q, const void* k, const void* v,
+                                 const float* logP, const float* beta, const float* state_pool,
+                                 int32_t n_slots, const int32_t* slot, const float* G,
+                                 const float* C, const int32_t* order, const int32_t* depth,
+                                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B,
+                                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, void* O, float* U,
+                                 uint32_t* err, void* stream);
+
+/*
+ * bole_factor_inverse - the factor producer of an explicit-inverse solve (an
+ * exact solve the closed form allows; arXiv page, Theorem 1 discussion).  It
+ * forms G and C as bole_factor_gc does, then W = (I + G)^-1 by repeated
+ * squaring, W = prod_{k : 2^k <= d_b} (I + (-G)^(2^k)) (the finite Neumann
+ * polynomial of Lemma 3 in ceil(log2(d_b + 1)) factors), and M = C W, so that a
+ * verify needs only U = W R and O = B0 + M R.
+ *
+ *  arguments as bole_factor_gc, with the outputs
+ *  out  W, M [B,H,64,64]  float32, level-order positions as G and C; W and M
+ *       are lower triangular, rows and columns >= T_b are exactly 0.  The
+ *       squaring and M's product run on bf16 MFMA with every operand split
+ *       hi + lo and float32 accumulation.
+ *  out  err               TREE_SIZE
+ * W and M take the G/C workspace (bole_gc_workspace_bytes).
+ */
+BOLE_API int bole_factor_inverse(int32_t dtype, const void* q, const void* k, const float* logP,
+                                 const float* beta, const uint64_t* anc, const int32_t* order,
+                                 const int32_t* tree_off, int32_t B, int32_t N, int32_t H,
+                                 int32_t d_k, float* W, float* M, uint32_t* err, void* stream);
+
+/*
+ * bole_verify_inverse - bole_verify for the explicit-inverse solve: with W and M
+ * from bole_factor_inverse it forms B0 and R as bole_verify does, then
+ * U = W R and O = B0 + M R (two independent products, no chain across row
+ * tiles).
+ *
+ *  arguments as bole_verify, with W and M in place of G and C; outputs and
+ *  errors as bole_verify.  tree_depth[] is read only to skip rejected trees.
+ */
+BOLE_API int bole_verify_inverse(int32_t dtype, const void* q, const void* k, const void* v,
+                                 const float* logP, const float* beta, const float* state_pool,
+                                 int32_t n_slots, const int32_t* slot, const float* W,
+                                 const float* M, const int32_t* order, const int32_t* depth,
+                                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B,
+                                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, void* O, float* U,
+                                 uint32_t* err, void* stream);
+
+/*
  * bole_factor_verify - bole_factor_gc and bole_verify in one launch.  With
  * d_v <= 128 a head's value columns form one workgroup, so the factors have a
  * single consumer; here the Gram products and their masked epilogue run inside

@@ -52,11 +52,13 @@ def lib() -> ctypes.CDLL:
         L.bole_tree_prep.argtypes = [P, P, i32, i32, P, i32, i32, P, P, P, P, P, P, P]
         L.bole_gc_workspace_bytes.restype = ctypes.c_size_t
         L.bole_gc_workspace_bytes.argtypes = [i32, i32]
-        L.bole_factor_gc.restype = ctypes.c_int
-        L.bole_factor_gc.argtypes = [i32, P, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, P]
-        L.bole_verify.restype = ctypes.c_int
-        L.bole_verify.argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P, P]
-                                  + [i32] * 5 + [P, P, P, P])
+        for fn in ("bole_factor_gc", "bole_factor_inverse"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = [i32, P, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, P]
+        for fn in ("bole_verify", "bole_verify_neumann", "bole_verify_inverse"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P, P]
+                                       + [i32] * 5 + [P, P, P, P])
         L.bole_factor_verify.restype = ctypes.c_int
         L.bole_factor_verify.argtypes = ([i32, P, P, P, P, P, P, i32, P, P, P, P, P, P]
                                          + [i32] * 5 + [P, P, P, P])
@@ -161,6 +163,16 @@ def bole_tree_prep(parent, tree_off, log_gamma, depth, anc, order, tree_depth, l
 
 
 def bole_factor_gc(q, k, logP, beta, anc, order, tree_off, G, C, err=None, stream=None):
+    _factor("bole_factor_gc", q, k, logP, beta, anc, order, tree_off, G, C, err, stream)
+
+
+def bole_factor_inverse(q, k, logP, beta, anc, order, tree_off, W, M, err=None, stream=None):
+    """Factor producer of the explicit-inverse solve: W = (I+G)^-1 and M = C W
+    in place of G and C (same shapes and layout)."""
+    _factor("bole_factor_inverse", q, k, logP, beta, anc, order, tree_off, W, M, err, stream)
+
+
+def _factor(fn, q, k, logP, beta, anc, order, tree_off, G, C, err, stream):
     _need(q, "q", (torch.float32, torch.bfloat16), 3)
     _need(k, "k", q.dtype, 3)
     N, H, d_k = q.shape
@@ -181,13 +193,33 @@ def bole_factor_gc(q, k, logP, beta, anc, order, tree_off, G, C, err=None, strea
         if tuple(t.shape) != (B, H, MAX_TREE, MAX_TREE):
             raise ValueError(f"{nm} must be [B, H, 64, 64]")
     _need(err, "err", torch.int32, 1, allow_none=True)
-    _check("bole_factor_gc", lib().bole_factor_gc(
+    _check(fn, getattr(lib(), fn)(
         _code(q.dtype), _ptr(q), _ptr(k), _ptr(logP), _ptr(beta), _ptr(anc), _ptr(order),
         _ptr(tree_off), B, N, H, d_k, _ptr(G), _ptr(C), _ptr(err), _stream(stream)))
 
 
 def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_off, tree_depth,
                 O, U, err=None, stream=None):
+    _verify("bole_verify", q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_off,
+            tree_depth, O, U, err, stream)
+
+
+def bole_verify_neumann(q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_off,
+                        tree_depth, O, U, err=None, stream=None):
+    """bole_verify solving by the d-step Neumann propagation."""
+    _verify("bole_verify_neumann", q, k, v, logP, beta, state_pool, slot, G, C, order, depth,
+            tree_off, tree_depth, O, U, err, stream)
+
+
+def bole_verify_inverse(q, k, v, logP, beta, state_pool, slot, W, M, order, depth, tree_off,
+                        tree_depth, O, U, err=None, stream=None):
+    """bole_verify with W and M from bole_factor_inverse in place of G and C."""
+    _verify("bole_verify_inverse", q, k, v, logP, beta, state_pool, slot, W, M, order, depth,
+            tree_off, tree_depth, O, U, err, stream)
+
+
+def _verify(fn, q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_off, tree_depth,
+            O, U, err, stream):
     _need(q, "q", (torch.float32, torch.bfloat16), 3)
     _need(k, "k", q.dtype, 3)
     _need(v, "v", q.dtype, 3)
@@ -221,7 +253,7 @@ def bole_verify(q, k, v, logP, beta, state_pool, slot, G, C, order, depth, tree_
     if slot.shape[0] != B or tree_depth.shape[0] != B:
         raise ValueError("slot and tree_depth need B entries")
     _need(err, "err", torch.int32, 1, allow_none=True)
-    _check("bole_verify", lib().bole_verify(
+    _check(fn, getattr(lib(), fn)(
         _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(logP), _ptr(beta), _ptr(state_pool),
         state_pool.shape[0], _ptr(slot), _ptr(G), _ptr(C), _ptr(order), _ptr(depth),
         _ptr(tree_off), _ptr(tree_depth), B, N, H, d_k, d_v, _ptr(O), _ptr(U), _ptr(err),

@@ -17,6 +17,19 @@ int bole_verify_launch(int32_t, const void*, const void*, const void*, const flo
                        const float*, const int32_t*, const int32_t*, const int32_t*,
                        const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
                        float*, uint32_t*, hipStream_t);
+int bole_verify_neumann_launch(int32_t, const void*, const void*, const void*, const float*,
+                               const float*, const float*, int32_t, const int32_t*, const float*,
+                               const float*, const int32_t*, const int32_t*, const int32_t*,
+                               const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                               float*, uint32_t*, hipStream_t);
+int bole_verify_inverse_launch(int32_t, const void*, const void*, const void*, const float*,
+                               const float*, const float*, int32_t, const int32_t*, const float*,
+                               const float*, const int32_t*, const int32_t*, const int32_t*,
+                               const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                               float*, uint32_t*, hipStream_t);
+int bole_factor_inverse_launch(int32_t, const void*, const void*, const float*, const float*,
+                               const uint64_t*, const int32_t*, const int32_t*, int32_t, int32_t,
+                               int32_t, int32_t, float*, float*, uint32_t*, hipStream_t);
 int bole_factor_verify_max_dk(int32_t);
 int bole_factor_verify_launch(int32_t, const void*, const void*, const void*, const float*,
                               const float*, const float*, int32_t, const int32_t*,
@@ -55,6 +68,44 @@ bool dtype_ok(int32_t dt) { return dt == BOLE_F32 || dt == BOLE_BF16; }
 // B * H * tiles must fit a 1-D grid
 bool grid_ok(int64_t B, int64_t H, int64_t tiles) { return B * H * tiles < kMaxGrid; }
 
+using VerifyLaunch = int (*)(int32_t, const void*, const void*, const void*, const float*,
+                             const float*, const float*, int32_t, const int32_t*, const float*,
+                             const float*, const int32_t*, const int32_t*, const int32_t*,
+                             const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
+                             float*, uint32_t*, hipStream_t);
+
+// bole_verify and its alternative solves share their argument checks
+int verify_checked(VerifyLaunch launch, int32_t dtype, const void* q, const void* k,
+                   const void* v, const float* logP, const float* beta, const float* state_pool,
+                   int32_t n_slots, const int32_t* slot, const float* G, const float* C,
+                   const int32_t* order, const int32_t* depth, const int32_t* tree_off,
+                   const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                   int32_t d_v, void* O, float* U, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !G || !C || !order || !depth ||
+      !tree_off || !tree_depth || !O || !U)
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 4)) return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return BOLE_E_UNSUPPORTED;
+  return launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, order, depth,
+                tree_off, tree_depth, B, N, H, d_k, d_v, O, U, err, (hipStream_t)stream);
+}
+
+using FactorLaunch = int (*)(int32_t, const void*, const void*, const float*, const float*,
+                             const uint64_t*, const int32_t*, const int32_t*, int32_t, int32_t,
+                             int32_t, int32_t, float*, float*, uint32_t*, hipStream_t);
+
+int factor_checked(FactorLaunch launch, int32_t dtype, const void* q, const void* k,
+                   const float* logP, const float* beta, const uint64_t* anc,
+                   const int32_t* order, const int32_t* tree_off, int32_t B, int32_t N,
+                   int32_t H, int32_t d_k, float* G, float* C, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !logP || !beta || !anc || !order || !tree_off || !G || !C) return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || !grid_ok(B, H, 1)) return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k)) return BOLE_E_UNSUPPORTED;
+  return launch(dtype, q, k, logP, beta, anc, order, tree_off, B, N, H, d_k, G, C, err,
+                (hipStream_t)stream);
+}
 }  // namespace
 
 extern "C" {
@@ -83,12 +134,8 @@ int bole_factor_gc(int32_t dtype, const void* q, const void* k, const float* log
                    const float* beta, const uint64_t* anc, const int32_t* order,
                    const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
                    float* G, float* C, uint32_t* err, void* stream) {
-  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
-  if (!q || !k || !logP || !beta || !anc || !order || !tree_off || !G || !C) return BOLE_E_NULL;
-  if (B < 1 || N < 1 || H < 1 || !grid_ok(B, H, 1)) return BOLE_E_SHAPE;
-  if (!head_dim_ok(d_k)) return BOLE_E_UNSUPPORTED;
-  return bole_factor_gc_launch(dtype, q, k, logP, beta, anc, order, tree_off, B, N, H, d_k, G,
-                               C, err, (hipStream_t)stream);
+  return factor_checked(bole_factor_gc_launch, dtype, q, k, logP, beta, anc, order, tree_off, B,
+                        N, H, d_k, G, C, err, stream);
 }
 
 int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
@@ -97,15 +144,39 @@ int bole_verify(int32_t dtype, const void* q, const void* k, const void* v, cons
                 const int32_t* tree_off, const int32_t* tree_depth, int32_t B, int32_t N,
                 int32_t H, int32_t d_k, int32_t d_v, void* O, float* U, uint32_t* err,
                 void* stream) {
-  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
-  if (!q || !k || !v || !logP || !beta || !state_pool || !slot || !G || !C || !order || !depth ||
-      !tree_off || !tree_depth || !O || !U)
-    return BOLE_E_NULL;
-  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || !grid_ok(B, H, 4)) return BOLE_E_SHAPE;
-  if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return BOLE_E_UNSUPPORTED;
-  return bole_verify_launch(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, order,
-                            depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U, err,
-                            (hipStream_t)stream);
+  return verify_checked(bole_verify_launch, dtype, q, k, v, logP, beta, state_pool, n_slots, slot,
+                        G, C, order, depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U, err,
+                        stream);
+}
+
+int bole_verify_neumann(int32_t dtype, const void* q, const void* k, const void* v,
+                        const float* logP, const float* beta, const float* state_pool,
+                        int32_t n_slots, const int32_t* slot, const float* G, const float* C,
+                        const int32_t* order, const int32_t* depth, const int32_t* tree_off,
+                        const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                        int32_t d_v, void* O, float* U, uint32_t* err, void* stream) {
+  return verify_checked(bole_verify_neumann_launch, dtype, q, k, v, logP, beta, state_pool,
+                        n_slots, slot, G, C, order, depth, tree_off, tree_depth, B, N, H, d_k,
+                        d_v, O, U, err, stream);
+}
+
+int bole_verify_inverse(int32_t dtype, const void* q, const void* k, const void* v,
+                        const float* logP, const float* beta, const float* state_pool,
+                        int32_t n_slots, const int32_t* slot, const float* W, const float* M,
+                        const int32_t* order, const int32_t* depth, const int32_t* tree_off,
+                        const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                        int32_t d_v, void* O, float* U, uint32_t* err, void* stream) {
+  return verify_checked(bole_verify_inverse_launch, dtype, q, k, v, logP, beta, state_pool,
+                        n_slots, slot, W, M, order, depth, tree_off, tree_depth, B, N, H, d_k,
+                        d_v, O, U, err, stream);
+}
+
+int bole_factor_inverse(int32_t dtype, const void* q, const void* k, const float* logP,
+                        const float* beta, const uint64_t* anc, const int32_t* order,
+                        const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                        float* W, float* M, uint32_t* err, void* stream) {
+  return factor_checked(bole_factor_inverse_launch, dtype, q, k, logP, beta, anc, order, tree_off,
+                        B, N, H, d_k, W, M, err, stream);
 }
 
 int bole_factor_verify(int32_t dtype, const void* q, const void* k, const void* v,

@@ -24,7 +24,16 @@
 //  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
 //           a permuted K order (load_tri_blocks) that makes the lane's own U
 //           tiles the B operand: U never leaves registers.
-//  Readout  O = B0 + C U, float32 accumulation.  Products that U and the
+//  Readout  O = B0 + C U, float32 accumulation.
+//
+// Two other exact solves can be selected (SOLVE):
+//  Neumann  the d_b-step propagation of Eq. 8 as the pages run it: Z <- -G Z,
+//           U += Z, starting from Z = U = R.  Z^(m) = (-G)^m R vanishes on rows
+//           shallower than m, so a step skips row tiles whose deepest row is
+//           above m and input tiles whose deepest row is above m - 1.
+//  Inverse  the G and C inputs hold W = (I + G)^-1 and M = C W (formed by
+//           bole_factor_inverse): U = W R and O = B0 + M R, two independent
+//           products with no chain between tiles.  Products that U and the
 //           committed state depend on split every float32 operand hi + lo; O's
 //           own (Q S_pre, C U) do so only for float32 tokens (kOExact).
 //  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
@@ -45,7 +54,7 @@ namespace bole {
 // the kernel derives the tree's topology and this head's gate sums itself from
 // the parents and log-gates, with the arithmetic of bole_tree_prep, and
 // publishes them for the commit; the order/depth/anc/logP inputs are unused.
-template <int DT, bool FUSED, bool ONE, bool PREP>
+template <int DT, bool FUSED, bool ONE, bool PREP, int SOLVE = kSolveBlocked>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ logP, const float* __restrict__ beta,
@@ -57,6 +66,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf, PrepIO prep,
     uint32_t* __restrict__ err) {
   using SC = StageCfg<DT>;
+  static_assert(!(FUSED && SOLVE == kSolveInverse), "W and M come from bole_factor_inverse");
   // O's own products (Q S_pre for B0, C U) carry the split low halves only for
   // float32 tokens; with bf16 tokens O is stored in bf16, and each product is
   // taken at that precision (hi parts: relative error near 2^-8, inside the
@@ -227,7 +237,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int mat = id >> 10, rem = id & 1023;
     const int row = rem >> 4, c4 = rem & 15;
     bf16x4 hi, lo;
-    split_bf16x4(mat ? gcr[it] : -gcr[it], hi, lo);
+    // the substitution and the propagation use -G; the inverse solve W as is
+    split_bf16x4(mat || SOLVE == kSolveInverse ? gcr[it] : -gcr[it], hi, lo);
     const int o = gc_pos(row, 4 * c4);
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat) * kGcPlane + o) = hi;
     *reinterpret_cast<bf16x4*>(gcs + (2 * mat + 1) * kGcPlane + o) = lo;
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // B layout of X Y) and as mfma(Y_B, X_A) (the transpose, i.e. the A layout of
   // X Y), so both operand forms of every factor are at hand.  Operands are
   // split bf16 hi + lo, three products each, float32 accumulation.
-  if (w < 4 && w < nmt) {
+  if (SOLVE == kSolveBlocked && w < 4 && w < nmt) {
     const int tb = 16 * w;
     const int k_span = rowDep[min(tb + 15, T - 1)] - rowDep[tb] + 1;
     auto id_entry = [&](int e) { return 4 * g4 + e == l16 ? 1.0f : 0.0f; };
@@ -536,58 +547,152 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
   }
 
-  // ---------------- Solve (I + G) U = R by 16-row tiles --------------------
-  // U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s).  The sum uses the 32-wide
-  // permuted blocks of -G with the tiles not yet solved entered as zeros; the
-  // lane's own U tiles are the B operand.  Tiles past the tree stay zero.
   f32x4 u[4];
+  if (SOLVE == kSolveBlocked) {
+    // ---------------- Solve (I + G) U = R by 16-row tiles --------------------
+    // U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s).  The sum uses the 32-wide
+    // permuted blocks of -G with the tiles not yet solved entered as zeros; the
+    // lane's own U tiles are the B operand.  Tiles past the tree stay zero.
 #pragma unroll
-  for (int t = 0; t < 4; ++t) u[t] = zero_f32x4();
+    for (int t = 0; t < 4; ++t) u[t] = zero_f32x4();
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < nmt) {
-      f32x4 y = ru[t];
+    for (int t = 0; t < 4; ++t) {
+      if (t < nmt) {
+        f32x4 y = ru[t];
 #pragma unroll
-      for (int J = 0; J <= t / 2; ++J) {
-        if (2 * J < t) {  // block J holds a solved tile
-          bf16x8 zh, zl;
-          split_pair(u[2 * J], 2 * J + 1 < t ? u[2 * J + 1] : zero_f32x4(), zh, zl);
-          const int o = gc_frag(16 * t + l16, J, g4);
-          const bf16x8 gh = *reinterpret_cast<const bf16x8*>(gcs + o);
-          const bf16x8 gl = *reinterpret_cast<const bf16x8*>(gcs + kGcPlane + o);
-          y = mfma_bf16(gh, zh, y);
-          y = mfma_bf16(gl, zh, y);
-          y = mfma_bf16(gh, zl, y);
+        for (int J = 0; J <= t / 2; ++J) {
+          if (2 * J < t) {  // block J holds a solved tile
+            bf16x8 zh, zl;
+            split_pair(u[2 * J], 2 * J + 1 < t ? u[2 * J + 1] : zero_f32x4(), zh, zl);
+            const int o = gc_frag(16 * t + l16, J, g4);
+            const bf16x8 gh = *reinterpret_cast<const bf16x8*>(gcs + o);
+            const bf16x8 gl = *reinterpret_cast<const bf16x8*>(gcs + kGcPlane + o);
+            y = mfma_bf16(gh, zh, y);
+            y = mfma_bf16(gl, zh, y);
+            y = mfma_bf16(gh, zl, y);
+          }
+        }
+        bf16x4 yh, yl;
+        split_bf16x4(y, yh, yl);
+        const bf16x4 ih = invs[t][0][lane], il = invs[t][1][lane];
+        f32x4 acc = mfma16_bf16(ih, yh, zero_f32x4());
+        acc = mfma16_bf16(il, yh, acc);
+        u[t] = mfma16_bf16(ih, yl, acc);
+      }
+    }
+
+  } else if (SOLVE == kSolveNeumann) {
+    // ------------- Neumann propagation: Z <- -G Z, U += Z, d_b steps -------------
+    // The product uses the same permuted 32-wide blocks of -G as the
+    // substitution (entries above the diagonal are zero), with the lane's own Z
+    // tiles as the B operand.  Tile depth bounds are uniform across the
+    // workgroup: the rows are shared, so no wave diverges.
+    int tmax[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tmax[t] = 16 * t < T ? rowDep[min(16 * t + 15, T - 1)] : -1;
+    // level order: the last row is the deepest (at most T - 1 in a valid tree;
+    // the bound keeps the loop short whatever the depth input holds)
+    const int dmax = min(rowDep[T - 1], T - 1);
+    // B0 waits in LDS while the propagation runs, at the lane's own positions
+    // of the U tile that is written there later (held in registers across the
+    // loop it would spill).  The V tile shares those bytes: every wave must be
+    // done reading it first.
+    float* park = reinterpret_cast<float*>(stage);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) park[vtile_idx(16 * t + 4 * g4 + e, vloc)] = qs[t][e];
+    asm volatile("" ::: "memory");
+    f32x4 z[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u[t] = ru[t];
+      z[t] = ru[t];
+    }
+    for (int m = 1; m <= dmax; ++m) {
+      bf16x8 zh[2], zl[2];
+#pragma unroll
+      for (int J = 0; J < 2; ++J) split_pair(z[2 * J], z[2 * J + 1], zh[J], zl[J]);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 y = zero_f32x4();
+        if (tmax[I] >= m) {
+#pragma unroll
+          for (int J = 0; J <= I / 2; ++J) {
+            if (max(tmax[2 * J], tmax[2 * J + 1]) >= m - 1) {
+              // re-read every step: held across the loop, the six blocks of
+              // -G would take 48 registers and spill
+              int o = gc_frag(16 * I + l16, J, g4);
+              asm volatile("" : "+v"(o));
+              const bf16x8 gh = *reinterpret_cast<const bf16x8*>(gcs + o);
+              const bf16x8 gl = *reinterpret_cast<const bf16x8*>(gcs + kGcPlane + o);
+              y = mfma_bf16(gh, zh[J], y);
+              y = mfma_bf16(gl, zh[J], y);
+              y = mfma_bf16(gh, zl[J], y);
+            }
+          }
+        }
+        z[I] = y;
+        u[I] += y;
+      }
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qs[t][e] = park[vtile_idx(16 * t + 4 * g4 + e, vloc)];
+  } else {
+    // ------------- Inverse: U = W R, O = B0 + M R -------------
+    bf16x8 rh[2], rl[2];
+#pragma unroll
+    for (int J = 0; J < 2; ++J) split_pair(ru[2 * J], ru[2 * J + 1], rh[J], rl[J]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 y = zero_f32x4(), acc = qs[I];
+      if (I < nmt) {
+#pragma unroll
+        for (int J = 0; J <= I / 2; ++J) {
+          const int o = gc_frag(16 * I + l16, J, g4);
+          const bf16x8 wh = *reinterpret_cast<const bf16x8*>(gcs + o);
+          const bf16x8 wl = *reinterpret_cast<const bf16x8*>(gcs + kGcPlane + o);
+          const bf16x8 mh = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
+          y = mfma_bf16(wh, rh[J], y);
+          y = mfma_bf16(wl, rh[J], y);
+          y = mfma_bf16(wh, rl[J], y);
+          acc = mfma_bf16(mh, rh[J], acc);
+          if (kOExact) {
+            const bf16x8 ml = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
+            acc = mfma_bf16(ml, rh[J], acc);
+            acc = mfma_bf16(mh, rl[J], acc);
+          }
         }
       }
-      bf16x4 yh, yl;
-      split_bf16x4(y, yh, yl);
-      const bf16x4 ih = invs[t][0][lane], il = invs[t][1][lane];
-      f32x4 acc = mfma16_bf16(ih, yh, zero_f32x4());
-      acc = mfma16_bf16(il, yh, acc);
-      u[t] = mfma16_bf16(ih, yl, acc);
+      u[I] = y;
+      qs[I] = acc;
     }
   }
-
-  // ---------------- Readout: O = B0 + C U ----------------
-  bf16x8 uh[2], ul[2];
+  if (SOLVE != kSolveInverse) {
+    // ---------------- Readout: O = B0 + C U ----------------
+    bf16x8 uh[2], ul[2];
 #pragma unroll
-  for (int J = 0; J < 2; ++J) split_pair(u[2 * J], u[2 * J + 1], uh[J], ul[J]);
+    for (int J = 0; J < 2; ++J) split_pair(u[2 * J], u[2 * J + 1], uh[J], ul[J]);
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    f32x4 acc = qs[I];  // plane rows past tile nmt are zero
+    for (int I = 0; I < 4; ++I) {
+      f32x4 acc = qs[I];  // plane rows past tile nmt are zero
 #pragma unroll
-    for (int J = 0; J <= I / 2; ++J) {
-      const int o = gc_frag(16 * I + l16, J, g4);
-      const bf16x8 ch = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
-      acc = mfma_bf16(ch, uh[J], acc);
-      if (kOExact) {  // bf16 tokens: C U at the precision O is stored in
-        const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
-        acc = mfma_bf16(cl, uh[J], acc);
-        acc = mfma_bf16(ch, ul[J], acc);
+      for (int J = 0; J <= I / 2; ++J) {
+        const int o = gc_frag(16 * I + l16, J, g4);
+        const bf16x8 ch = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
+        acc = mfma_bf16(ch, uh[J], acc);
+        if (kOExact) {  // bf16 tokens: C U at the precision O is stored in
+          const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
+          acc = mfma_bf16(cl, uh[J], acc);
+          acc = mfma_bf16(ch, ul[J], acc);
+        }
       }
+      qs[I] = acc;
     }
-    qs[I] = acc;
   }
 
   // ---------------- Store U and O through LDS ----------------
@@ -645,7 +750,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 }  // namespace bole
 
 namespace {
-template <int DT, bool FUSED, bool ONE, bool PREP = false>
+template <int DT, bool FUSED, bool ONE, bool PREP = false, int SOLVE = bole::kSolveBlocked>
 int launch_verify_t(const void* q, const void* k, const void* v, const float* logP,
                     const float* beta, const float* state_pool, int32_t n_slots,
                     const int32_t* slot, const float* G, const float* C, const uint64_t* anc,
@@ -659,13 +764,13 @@ int launch_verify_t(const void* q, const void* k, const void* v, const float* lo
   const bool v_ok = d_v % (16 / esize) == 0 && (uintptr_t)v % 16 == 0;
   const bool out_ok = d_v % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)O % (4 * esize) == 0;
   const int vecf = (v_ok ? bole::kVecV : 0) | (out_ok ? bole::kVecOut : 0);
-  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP>), grid, block, 0, s, q, k, v,
+  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE>), grid, block, 0, s, q, k, v,
                      logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
                      tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err);
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 
-template <bool FUSED>
+template <bool FUSED, int SOLVE = bole::kSolveBlocked>
 int launch_verify(int32_t dtype, const void* q, const void* k, const void* v, const float* logP,
                   const float* beta, const float* state_pool, int32_t n_slots,
                   const int32_t* slot, const float* G, const float* C, const uint64_t* anc,
@@ -677,12 +782,12 @@ int launch_verify(int32_t dtype, const void* q, const void* k, const void* v, co
       B, N, H, d_k, d_v, O, U, err, s
   if (dtype == BOLE_BF16) {
     if (FUSED || d_k <= bole::StageCfg<BOLE_BF16>::KC)
-      return launch_verify_t<BOLE_BF16, FUSED, true>(BOLE_VERIFY_ARGS);
-    return launch_verify_t<BOLE_BF16, false, false>(BOLE_VERIFY_ARGS);
+      return launch_verify_t<BOLE_BF16, FUSED, true, false, SOLVE>(BOLE_VERIFY_ARGS);
+    return launch_verify_t<BOLE_BF16, false, false, false, SOLVE>(BOLE_VERIFY_ARGS);
   }
   if (FUSED || d_k <= bole::StageCfg<BOLE_F32>::KC)
-    return launch_verify_t<BOLE_F32, FUSED, true>(BOLE_VERIFY_ARGS);
-  return launch_verify_t<BOLE_F32, false, false>(BOLE_VERIFY_ARGS);
+    return launch_verify_t<BOLE_F32, FUSED, true, false, SOLVE>(BOLE_VERIFY_ARGS);
+  return launch_verify_t<BOLE_F32, false, false, false, SOLVE>(BOLE_VERIFY_ARGS);
 #undef BOLE_VERIFY_ARGS
 }
 }  // namespace
@@ -697,6 +802,36 @@ extern "C" int bole_verify_launch(int32_t dtype, const void* q, const void* k, c
   return launch_verify<false>(dtype, q, k, v, logP, beta, state_pool, n_slots, slot, G, C,
                               nullptr, order, depth, tree_off, tree_depth, B, N, H, d_k, d_v, O,
                               U, err, s);
+}
+
+extern "C" int bole_verify_neumann_launch(int32_t dtype, const void* q, const void* k,
+                                          const void* v, const float* logP, const float* beta,
+                                          const float* state_pool, int32_t n_slots,
+                                          const int32_t* slot, const float* G, const float* C,
+                                          const int32_t* order, const int32_t* depth,
+                                          const int32_t* tree_off, const int32_t* tree_depth,
+                                          int32_t B, int32_t N, int32_t H, int32_t d_k,
+                                          int32_t d_v, void* O, float* U, uint32_t* err,
+                                          hipStream_t s) {
+  return launch_verify<false, bole::kSolveNeumann>(dtype, q, k, v, logP, beta, state_pool,
+                                                   n_slots, slot, G, C, nullptr, order, depth,
+                                                   tree_off, tree_depth, B, N, H, d_k, d_v, O, U,
+                                                   err, s);
+}
+
+extern "C" int bole_verify_inverse_launch(int32_t dtype, const void* q, const void* k,
+                                          const void* v, const float* logP, const float* beta,
+                                          const float* state_pool, int32_t n_slots,
+                                          const int32_t* slot, const float* W, const float* M,
+                                          const int32_t* order, const int32_t* depth,
+                                          const int32_t* tree_off, const int32_t* tree_depth,
+                                          int32_t B, int32_t N, int32_t H, int32_t d_k,
+                                          int32_t d_v, void* O, float* U, uint32_t* err,
+                                          hipStream_t s) {
+  return launch_verify<false, bole::kSolveInverse>(dtype, q, k, v, logP, beta, state_pool,
+                                                   n_slots, slot, W, M, nullptr, order, depth,
+                                                   tree_off, tree_depth, B, N, H, d_k, d_v, O, U,
+                                                   err, s);
 }
 
 extern "C" int bole_factor_verify_max_dk(int32_t dtype) {

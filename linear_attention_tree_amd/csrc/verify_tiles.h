@@ -60,6 +60,14 @@ struct PrepIO {
   float* logP;            // [N, H] of the layer
 };
 
+// How the verify kernel solves (I + G) U = R.  All three are exact (the closed
+// form fixes the outputs, not the solve; arXiv page, Theorem 1 discussion).
+//  kSolveBlocked  forward substitution over 16-row tiles with the diagonal
+//                 blocks' inverses formed while the state streams in
+//  kSolveNeumann  the d_b-step propagation Z <- -G Z, U += Z of Eq. 8
+//  kSolveInverse  the G and C inputs hold W = (I + G)^-1 and M = C W
+constexpr int kSolveBlocked = 0, kSolveNeumann = 1, kSolveInverse = 2;
+
 // Bit flags of the value-tile transfers, set by the host.
 // kVecV: d_v is a multiple of the elements in 16 bytes of v and v is 16-byte
 // aligned, so V rows move as 16-byte pieces.  kVecOut: d_v % 4 == 0 and U and O

@@ -60,12 +60,19 @@ class TreeRound:
                             t.tree_depth, logP, self.err, stream)
         return logP
 
-    def factor(self, q, k, logP, beta, stream=None):
-        t = self.topo
-        bole.bole_factor_gc(q, k, logP, beta, t.anc, t.order, t.tree_off, self.G, self.C, self.err,
-                            stream)
+    # the two-call path's exact solves: (producer, verify) of each
+    SOLVES = {"blocked": ("bole_factor_gc", "bole_verify"),
+              "neumann": ("bole_factor_gc", "bole_verify_neumann"),
+              "inverse": ("bole_factor_inverse", "bole_verify_inverse")}
 
-    def verify(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None):
+    def factor(self, q, k, logP, beta, stream=None, solve="blocked"):
+        """G and C into the workspace (W and M for solve="inverse")."""
+        t = self.topo
+        getattr(bole, self.SOLVES[solve][0])(q, k, logP, beta, t.anc, t.order, t.tree_off, self.G,
+                                             self.C, self.err, stream)
+
+    def verify(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None,
+               solve="blocked"):
         t = self.topo
         N, H, _ = q.shape
         d_v = v.shape[2]
@@ -73,17 +80,22 @@ class TreeRound:
             O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
         if U is None:
             U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
-        bole.bole_verify(q, k, v, logP, beta, state_pool, slot, self.G, self.C, t.order, t.depth,
-                         t.tree_off, t.tree_depth, O, U, self.err, stream)
+        getattr(bole, self.SOLVES[solve][1])(q, k, v, logP, beta, state_pool, slot, self.G,
+                                             self.C, t.order, t.depth, t.tree_off, t.tree_depth,
+                                             O, U, self.err, stream)
         return O, U
 
     def layer(self, q, k, v, logP, beta, state_pool, slot, O=None, U=None, stream=None,
-              fused=False):
+              fused=False, solve="blocked"):
         """Factor producer then value-tiled verify for one layer (or both in one
-        launch with fused=True)."""
+        launch with fused=True).  solve picks the two-call path's solve of
+        (I+G) U = R: "blocked" substitution, the d-step "neumann" propagation,
+        or the explicit "inverse"."""
         if not fused:
-            self.factor(q, k, logP, beta, stream)
-            return self.verify(q, k, v, logP, beta, state_pool, slot, O, U, stream)
+            self.factor(q, k, logP, beta, stream, solve)
+            return self.verify(q, k, v, logP, beta, state_pool, slot, O, U, stream, solve)
+        if solve != "blocked":
+            raise ValueError("the fused verify solves by blocked substitution only")
         t = self.topo
         N, H, _ = q.shape
         d_v = v.shape[2]

@@ -132,13 +132,14 @@ def offset_copy(t, dtype=None):
 
 
 def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, misalign=False,
-              tree=False):
+              tree=False, solve="blocked"):
     """Run prep, factor, verify (and commit) on the GPU through the C ABI.
 
     fused: bole_factor_verify after bole_tree_prep; tree: bole_tree_verify per
     layer (preparation inside the verify launch).  misalign: v, O and U live one
     element past an aligned address (the kernels' element-wise fallbacks).
-    Returns dict with per-layer O, U (numpy float64), the state pools after
+    solve: the two-call path's solve ("blocked", "neumann" or "inverse"; G and
+    C in the result then hold W and M).  Returns dict with per-layer O, U (numpy float64), the state pools after
     commit, the prep outputs and the error word."""
     import torch
     from linear_attention_tree_amd import TreeRound
@@ -162,7 +163,7 @@ def gpu_round(case: Case, layers=None, commit=True, device="cuda", fused=False, 
                                      U=U, logP=logP[li])
         else:
             O, U = rnd.layer(d["q"], d["k"], v, logP[li], d["beta"], pools[li], slot, O=O, U=U,
-                             fused=fused)
+                             fused=fused, solve=solve)
         Os.append(O)
         Us.append(U)
     out = dict(logP=logP.cpu().numpy(), depth=rnd.topo.depth.cpu().numpy(),

@@ -34,6 +34,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_symbols()
     assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
                           "bole_verify", "bole_factor_verify", "bole_tree_verify",
+                          "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
                           "bole_commit_path", "bole_tree_conv", "bole_conv_commit",
                           "bole_status_string"}
     for n in names:
@@ -43,6 +44,8 @@ def test_exports_every_declared_symbol(L):
 
 def test_internal_launchers_are_hidden(L):
     for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch",
+              "bole_verify_neumann_launch", "bole_verify_inverse_launch",
+              "bole_factor_inverse_launch",
               "bole_tree_verify_launch", "bole_tree_conv_launch", "bole_conv_commit_launch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
@@ -66,8 +69,9 @@ def test_tree_prep_argument_errors(L):
     assert f(FAKE, FAKE, 1, 1, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == E_SHAPE
 
 
-def test_factor_gc_argument_errors(L):
-    f = L.bole_factor_gc
+@pytest.mark.parametrize("fn", ["bole_factor_gc", "bole_factor_inverse"])
+def test_factor_gc_argument_errors(L, fn):
+    f = getattr(L, fn)
     args = [FAKE] * 7
     assert f(7, *args, 1, 1, 1, 128, FAKE, FAKE, None, None) == E_DTYPE
     assert f(1, None, *args[1:], 1, 1, 1, 128, FAKE, FAKE, None, None) == E_NULL
@@ -76,19 +80,20 @@ def test_factor_gc_argument_errors(L):
         assert f(1, *args, 1, 1, 1, dk, FAKE, FAKE, None, None) == E_UNSUPPORTED
 
 
-def _verify(L, dtype=1, B=1, N=1, H=1, dk=128, dv=128, n_slots=1, O=FAKE):
+def _verify(L, dtype=1, B=1, N=1, H=1, dk=128, dv=128, n_slots=1, O=FAKE, fn="bole_verify"):
     p = [FAKE] * 6
-    return L.bole_verify(dtype, *p, n_slots, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    return getattr(L, fn)(dtype, *p, n_slots, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          B, N, H, dk, dv, O, FAKE, None, None)
 
 
-def test_verify_argument_errors(L):
-    assert _verify(L, dtype=2) == E_DTYPE
-    assert _verify(L, O=None) == E_NULL
-    assert _verify(L, B=0) == E_SHAPE
-    assert _verify(L, n_slots=0) == E_SHAPE
-    assert _verify(L, dv=100) == E_UNSUPPORTED
-    assert _verify(L, dk=512) == E_UNSUPPORTED
+@pytest.mark.parametrize("fn", ["bole_verify", "bole_verify_neumann", "bole_verify_inverse"])
+def test_verify_argument_errors(L, fn):
+    assert _verify(L, dtype=2, fn=fn) == E_DTYPE
+    assert _verify(L, O=None, fn=fn) == E_NULL
+    assert _verify(L, B=0, fn=fn) == E_SHAPE
+    assert _verify(L, n_slots=0, fn=fn) == E_SHAPE
+    assert _verify(L, dv=100, fn=fn) == E_UNSUPPORTED
+    assert _verify(L, dk=512, fn=fn) == E_UNSUPPORTED
 
 
 def test_factor_verify_argument_errors(L):
