@@ -18,8 +18,11 @@ Two independent formulations live here:
   for the G/C factors.
 * ``tree_conv`` (numpy): the tree-parallel short causal convolution of the
   pipeline's first stage and its conv-state commit, one node at a time.
+* ``forest`` (Python/numpy): budget selection by cumulative draft probability
+  and the packed-forest builder, one candidate at a time.
 
-Pins of the oracle itself are in tests/test_oracle.py and tests/test_oracle_conv.py.
+Pins of the oracle itself are in tests/test_oracle.py, tests/test_oracle_conv.py and
+tests/test_oracle_forest.py.
 """
 
 from __future__ import annotations
@@ -34,6 +37,7 @@ import numpy as np
 from .closed_form import (closed_form_tree, commit_closed_form, inverse_factors,  # noqa: F401
                           tree_factors)
 from .tree_conv import conv_commit, tree_conv  # noqa: F401
+from .forest import build_forest  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bole_oracle.c")

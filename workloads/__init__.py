@@ -401,3 +401,59 @@ def make_conv(cfg: Config, N: int, n_slots: int, C: Optional[int] = None, W: int
     b = (0.1 * rng.standard_normal(C)).astype(np.float32)
     return ConvInputs(x=to_storage(x, cfg.dtype), weight=w, bias=b,
                       state=to_storage(st, cfg.dtype), dtype=cfg.dtype)
+
+
+# ----------------------------------------------------------------------------
+# drafted candidate trees for budget selection
+
+STREAM_DRAFT = 5
+DRAFT_DEPTH = 8   # the pages' maximum draft depth
+DRAFT_TOPK = 4    # and their top-k
+
+
+@dataclass
+class Candidates:
+    """Drafted candidate trees of B requests, packed CSR-style: cand_parent
+    [M_total] (local parent, -1 for the root), p_draft [M_total] float32 (the
+    drafter's conditional probability of each candidate given its parent; 1 for
+    the root, the token the request already holds), cand_off [B+1]."""
+    cand_parent: np.ndarray
+    p_draft: np.ndarray
+    cand_off: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return len(self.cand_off) - 1
+
+
+def draft_tree(rng: np.random.Generator, depth: int = DRAFT_DEPTH, topk: int = DRAFT_TOPK,
+               vocab: int = 32, sigma: float = 2.0):
+    """One drafted candidate tree: the root gets topk children; at every further
+    level the first topk nodes of the level before (earlier parents first,
+    siblings in descending p) get topk children each.  A node's children carry
+    the topk largest probabilities of a softmax over vocab N(0, sigma^2) logits,
+    in descending order.  Nodes are numbered level by level."""
+    parent, p = [-1], [1.0]
+    level = [0]
+    for _ in range(depth):
+        nxt = []
+        for u in level[:topk]:
+            z = rng.standard_normal(vocab) * sigma
+            e = np.exp(z - z.max())
+            probs = np.sort(e / e.sum())[::-1][:topk]
+            for q in probs:
+                parent.append(u)
+                p.append(float(q))
+                nxt.append(len(parent) - 1)
+        level = nxt
+    return np.array(parent, np.int32), np.array(p, np.float32)
+
+
+def make_candidates(B: int, seed: int = 0, depth: int = DRAFT_DEPTH,
+                    topk: int = DRAFT_TOPK) -> Candidates:
+    rng = np.random.default_rng(np.random.SeedSequence([seed, B, STREAM_DRAFT, depth, topk]))
+    trees = [draft_tree(rng, depth, topk) for _ in range(B)]
+    off = np.zeros(B + 1, np.int32)
+    off[1:] = np.cumsum([len(t[0]) for t in trees])
+    return Candidates(cand_parent=np.concatenate([t[0] for t in trees]),
+                      p_draft=np.concatenate([t[1] for t in trees]), cand_off=off)
