@@ -393,6 +393,21 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     return ms, nbytes
 
 
+def time_forest_build(cfg, torch, ForestBuilder, dev, reps, capacity):
+    """Budget selection and packing for the workload's requests: drafted
+    candidate trees (depth 8, top-k 4) of cfg.B requests, the given forest
+    capacity, at most 64 nodes per request.  Returns ms per call (two launches)."""
+    c = W.make_candidates(cfg.B, seed=77)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    cp, pd, co = d(c.cand_parent), d(c.p_draft), d(c.cand_off)
+    fb = ForestBuilder(c.B, len(c.cand_parent), capacity, device=dev)
+    n_in = 16
+    g = capture(torch, lambda: [fb.build(cp, pd, co) for _ in range(n_in)])
+    ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
+    assert int(fb.err.item()) == 0, "device error bits set"
+    return ms, int(c.cand_off[-1]), int(fb.tree_off[-1].item())
+
+
 def commit_algorithmic_bytes(forest, L, H, d_k, d_v, e):
     """Compulsory HBM bytes of one commit over L layers: every committed slot
     read and written once (float32), plus the accepted path's key and U rows."""
@@ -651,6 +666,11 @@ def main():
                                               for i in range(n_in)])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     conv_ms, conv_bytes = time_tree_conv(cfg, sets, torch, bole, dev, K)
+    from linear_attention_tree_amd import ForestBuilder
+    forest_runs = {}
+    for cap in (cfg.B * cfg.T, 768):
+        f_ms, m_total, packed = time_forest_build(cfg, torch, ForestBuilder, dev, K, cap)
+        forest_runs[str(cap)] = {"ms": f_ms, "nodes_packed": packed}
     for s_ in sets:
         assert s_.rnd.error_bits() == 0, "device error bits set"
     dominant, bytes_fn = DOMINANT[args.path]
@@ -692,6 +712,12 @@ def main():
                 "achieved_GBs": conv_bytes / (conv_ms * 1e-3) / 1e9,
                 "frac_of_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "algorithmic_bytes_per_launch": conv_bytes,
+            },
+            "forest_build": {
+                "note": "budget selection by cumulative draft probability and forest packing "
+                        "(two launches), not part of the step; latency-bound",
+                "requests": cfg.B, "candidates": m_total, "max_tree": 64,
+                "by_capacity": forest_runs,
             },
         },
         "roofline": {

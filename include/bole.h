@@ -69,6 +69,8 @@ typedef enum {
 #define BOLE_ERR_TREE_SIZE 4u  /* tree_off range empty, larger than 64 or outside [0, N) */
 #define BOLE_ERR_BAD_ACCEPT 8u /* accepted node outside [-1, T_b) */
 #define BOLE_ERR_BAD_SLOT 16u  /* state slot outside [0, n_slots) */
+#define BOLE_ERR_BAD_PROB 32u  /* a draft probability outside [0, 1] or NaN */
+#define BOLE_ERR_DISCONNECTED 64u /* a packed node's parent is not an earlier node of its tree */
 
 #define BOLE_MAX_TREE 64
 
@@ -334,6 +336,53 @@ BOLE_API int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_
                      int64_t logp_layer_stride, const uint64_t* anc, const int32_t* tree_off,
                      const int32_t* accept, int32_t B, int32_t N, int32_t H, int32_t d_k,
                      int32_t d_v, uint32_t* err, void* stream);
+
+/*
+ * bole_forest_build - budget selection and the packed-forest builder (review
+ * page, section 三: the hardware-aware verification budget and the SGLang
+ * integration paragraphs).  Each drafted candidate v is scored with its path's
+ * cumulative draft probability rho(v) = prod over the root-to-v path of
+ * p_draft(u | parent(u)), taken as a float32 running product root first
+ * (rho(root) = p_draft(root)).  Candidates are ranked by rho descending, then
+ * depth, request and candidate index ascending, and taken in that order while
+ * the forest holds fewer than `capacity` nodes and the request fewer than
+ * `max_tree`.  With 0 <= p <= 1 a child never outranks its parent, so every
+ * request's selection is prefix-connected (checked: DISCONNECTED).  A request's
+ * selected nodes are numbered in rank order (root 0, parents first) and the
+ * requests packed in order: the result is the parent / tree_off input of
+ * bole_tree_prep and the verify calls.
+ *
+ *  in   cand_parent[M_total]  local parent of each candidate within its
+ *                             request's candidate tree, -1 for the root
+ *  in   p_draft[M_total]      float32 conditional draft probability (root: the
+ *                             token the request already holds, normally 1)
+ *  in   cand_off[B+1]         request b owns candidates [cand_off[b],
+ *                             cand_off[b+1]), at most 1024 of them
+ *  in   capacity, max_tree    forest capacity (>= 1) and per-request limit
+ *                             (1..64)
+ *  out  rho[M_total]          float32 score of every candidate (0 for a
+ *                             rejected request)
+ *  out  parent[capacity]      local parent of each packed node, -1 for roots
+ *                             and for slots past the last node
+ *  out  cand_of[capacity]     global candidate index of each packed node, -1
+ *                             past the last node
+ *  out  tree_off[B+1]         packed forest offsets (a request with no node
+ *                             gets an empty range)
+ *  in   workspace             bole_forest_workspace_bytes(B, max_tree) bytes
+ *                             of device scratch, 8-byte aligned
+ *  out  err                   BAD_PARENT, CYCLE, BAD_PROB, TREE_SIZE (more
+ *                             than 1024 candidates or offsets out of range):
+ *                             that request contributes no node; DISCONNECTED
+ * Limits: 1 <= B <= 4095, B * max_tree <= 16384 (BOLE_E_SHAPE otherwise).
+ * Two launches (per-request scoring and ranking, then one workgroup for the
+ * global cut and the packing).
+ */
+BOLE_API size_t bole_forest_workspace_bytes(int32_t B, int32_t max_tree);
+BOLE_API int bole_forest_build(const int32_t* cand_parent, const float* p_draft,
+                               const int32_t* cand_off, int32_t B, int32_t M_total,
+                               int32_t capacity, int32_t max_tree, float* rho, int32_t* parent,
+                               int32_t* cand_of, int32_t* tree_off, void* workspace,
+                               uint32_t* err, void* stream);
 
 /* Static description of a bole_status code. */
 BOLE_API const char* bole_status_string(int code);

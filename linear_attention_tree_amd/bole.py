@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libbole.so")
 
 BOLE_F32, BOLE_BF16 = 0, 1
 ERR_BAD_PARENT, ERR_CYCLE, ERR_TREE_SIZE, ERR_BAD_ACCEPT, ERR_BAD_SLOT = 1, 2, 4, 8, 16
+ERR_BAD_PROB, ERR_DISCONNECTED = 32, 64
 MAX_TREE = 64
 
 _lib = None
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.bole_commit_path.restype = ctypes.c_int
         L.bole_commit_path.argtypes = [i32, P, i64, i32, P, i32, P, i64, P, i64, P, i64, P, P,
                                        P, i32, i32, i32, i32, i32, P, P]
+        L.bole_forest_workspace_bytes.restype = ctypes.c_size_t
+        L.bole_forest_workspace_bytes.argtypes = [i32, i32]
+        L.bole_forest_build.restype = ctypes.c_int
+        L.bole_forest_build.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.bole_status_string.restype = ctypes.c_char_p
         L.bole_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -434,3 +439,41 @@ def bole_commit_path(state_pool, slot, k, U, logP, anc, tree_off, accept, err=No
         L, _ptr(sp), sp.stride(0), n_slots, _ptr(slot), _code(kk.dtype), _ptr(kk), kk.stride(0),
         _ptr(uu), uu.stride(0), _ptr(lp), lp.stride(0), _ptr(anc), _ptr(tree_off), _ptr(accept),
         B, N, H, d_k, d_v, _ptr(err), _stream(stream)))
+
+
+def bole_forest_workspace_bytes(B: int, max_tree: int) -> int:
+    return int(lib().bole_forest_workspace_bytes(B, max_tree))
+
+
+def bole_forest_build(cand_parent, p_draft, cand_off, capacity, max_tree, rho, parent, cand_of,
+                      tree_off, workspace, err=None, stream=None):
+    """Budget selection by cumulative draft probability and the packed forest
+    (see bole.h).  cand_parent [M_total] int32, p_draft [M_total] float32,
+    cand_off [B+1] int32; outputs rho [M_total] float32, parent and cand_of
+    [capacity] int32, tree_off [B+1] int32; workspace uint8 of at least
+    bole_forest_workspace_bytes(B, max_tree) bytes."""
+    _need(cand_parent, "cand_parent", torch.int32, 1)
+    _need(p_draft, "p_draft", torch.float32, 1)
+    _need(cand_off, "cand_off", torch.int32, 1)
+    M_total = cand_parent.shape[0]
+    B = cand_off.shape[0] - 1
+    if p_draft.shape[0] != M_total:
+        raise ValueError("p_draft must match cand_parent")
+    _need(rho, "rho", torch.float32, 1)
+    if rho.shape[0] != M_total:
+        raise ValueError("rho needs M_total entries")
+    for t, nm in ((parent, "parent"), (cand_of, "cand_of")):
+        _need(t, nm, torch.int32, 1)
+        if t.shape[0] != capacity:
+            raise ValueError(f"{nm} needs capacity entries")
+    _need(tree_off, "tree_off", torch.int32, 1)
+    if tree_off.shape[0] != B + 1:
+        raise ValueError("tree_off needs B + 1 entries")
+    _need(workspace, "workspace", torch.uint8, 1)
+    if workspace.numel() < bole_forest_workspace_bytes(B, max_tree):
+        raise ValueError("workspace too small")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_forest_build", lib().bole_forest_build(
+        _ptr(cand_parent), _ptr(p_draft), _ptr(cand_off), B, M_total, int(capacity),
+        int(max_tree), _ptr(rho), _ptr(parent), _ptr(cand_of), _ptr(tree_off), _ptr(workspace),
+        _ptr(err), _stream(stream)))

@@ -47,6 +47,9 @@ int bole_tree_conv_launch(int32_t, const void*, const float*, const float*, cons
 int bole_conv_commit_launch(int32_t, void*, int32_t, const int32_t*, const void*, const int32_t*,
                             const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
                             uint32_t*, hipStream_t);
+int bole_forest_build_launch(const int32_t*, const float*, const int32_t*, int32_t, int32_t,
+                             int32_t, int32_t, float*, int32_t*, int32_t*, int32_t*, void*,
+                             uint32_t*, hipStream_t);
 int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
@@ -60,6 +63,16 @@ constexpr int32_t kMaxGrid = 1 << 30;
 bool head_dim_ok(int32_t d) { return d >= 16 && d <= 256 && d % 16 == 0; }
 
 constexpr int32_t kMaxConvWidth = 8;
+
+// budget selection: request ids fit the order key's 12-bit field, and the
+// listed keys (B * max_tree) stay within one workgroup's reach
+constexpr int32_t kMaxForestRequests = 4095;
+constexpr int64_t kMaxForestListed = 16384;
+
+bool forest_shape_ok(int32_t B, int32_t max_tree) {
+  return B >= 1 && B <= kMaxForestRequests && max_tree >= 1 && max_tree <= BOLE_MAX_TREE &&
+         (int64_t)B * max_tree <= kMaxForestListed;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -243,6 +256,25 @@ int bole_conv_commit(int32_t dtype, void* conv_state, int32_t n_slots, const int
   if (W == 1) return BOLE_OK;  // no state to move
   return bole_conv_commit_launch(dtype, conv_state, n_slots, slot, x, parent, tree_off, accept, B,
                                  N, C, W, err, (hipStream_t)stream);
+}
+
+size_t bole_forest_workspace_bytes(int32_t B, int32_t max_tree) {
+  if (!forest_shape_ok(B, max_tree)) return 0;
+  return (size_t)12 * B * max_tree;  // a key and a parent position per listed slot
+}
+
+int bole_forest_build(const int32_t* cand_parent, const float* p_draft, const int32_t* cand_off,
+                      int32_t B, int32_t M_total, int32_t capacity, int32_t max_tree, float* rho,
+                      int32_t* parent, int32_t* cand_of, int32_t* tree_off, void* workspace,
+                      uint32_t* err, void* stream) {
+  if (!cand_parent || !p_draft || !cand_off || !rho || !parent || !cand_of || !tree_off ||
+      !workspace)
+    return BOLE_E_NULL;
+  if (!forest_shape_ok(B, max_tree) || M_total < 1 || capacity < 1) return BOLE_E_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return BOLE_E_UNSUPPORTED;
+  return bole_forest_build_launch(cand_parent, p_draft, cand_off, B, M_total, capacity, max_tree,
+                                  rho, parent, cand_of, tree_off, workspace, err,
+                                  (hipStream_t)stream);
 }
 
 int bole_commit_path(int32_t L, float* state_pool, int64_t state_layer_stride, int32_t n_slots,

@@ -133,3 +133,29 @@ class TreeRound:
 
     def error_bits(self) -> int:
         return int(self.err.item()) & 0xFFFFFFFF
+
+
+class ForestBuilder:
+    """Budget selection and forest packing into fixed-capacity buffers (their
+    addresses do not change from round to round, so a captured graph can reuse
+    them)."""
+
+    def __init__(self, B: int, M_total: int, capacity: int, max_tree: int = bole.MAX_TREE,
+                 device="cuda", err: Optional[torch.Tensor] = None):
+        dev = torch.device(device)
+        self.capacity, self.max_tree = capacity, max_tree
+        self.rho = torch.empty(M_total, dtype=torch.float32, device=dev)
+        self.parent = torch.empty(capacity, dtype=torch.int32, device=dev)
+        self.cand_of = torch.empty(capacity, dtype=torch.int32, device=dev)
+        self.tree_off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        nbytes = bole.bole_forest_workspace_bytes(B, max_tree)
+        if nbytes == 0:
+            raise ValueError("forest shape out of range")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.err = err if err is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def build(self, cand_parent, p_draft, cand_off, stream=None):
+        bole.bole_forest_build(cand_parent, p_draft, cand_off, self.capacity, self.max_tree,
+                               self.rho, self.parent, self.cand_of, self.tree_off,
+                               self.workspace, self.err, stream)
+        return self.parent, self.tree_off, self.cand_of

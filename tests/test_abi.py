@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(L):
                           "bole_verify", "bole_factor_verify", "bole_tree_verify",
                           "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
                           "bole_commit_path", "bole_tree_conv", "bole_conv_commit",
+                          "bole_forest_build", "bole_forest_workspace_bytes",
                           "bole_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -45,7 +46,7 @@ def test_exports_every_declared_symbol(L):
 def test_internal_launchers_are_hidden(L):
     for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch",
               "bole_verify_neumann_launch", "bole_verify_inverse_launch",
-              "bole_factor_inverse_launch",
+              "bole_factor_inverse_launch", "bole_forest_build_launch",
               "bole_tree_verify_launch", "bole_tree_conv_launch", "bole_conv_commit_launch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
@@ -182,3 +183,25 @@ def test_binding_rejects_host_tensors():
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         lat.bole_tree_prep(t, t, None, t, t.long(), t, t, None)
+
+
+def test_forest_build_argument_errors(L):
+    f = L.bole_forest_build
+    ws = ctypes.c_void_p(0x1000)
+
+    def call(B=2, M=10, cap=8, mt=64, ws=ws, rho=FAKE):
+        return f(FAKE, FAKE, FAKE, B, M, cap, mt, rho, FAKE, FAKE, FAKE, ws, None, None)
+
+    assert call(rho=None) == E_NULL
+    assert call(ws=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(B=4096) == E_SHAPE
+    assert call(M=0) == E_SHAPE
+    assert call(cap=0) == E_SHAPE
+    assert call(mt=0) == E_SHAPE
+    assert call(mt=65) == E_SHAPE
+    assert call(B=257, mt=64) == E_SHAPE                     # more than 16384 listed keys
+    assert call(ws=ctypes.c_void_p(0x1004)) == E_UNSUPPORTED  # workspace not 8-byte aligned
+    assert lat.bole_forest_workspace_bytes(16, 64) == 12 * 16 * 64
+    assert lat.bole_forest_workspace_bytes(0, 64) == 0
+    assert lat.bole_forest_workspace_bytes(300, 64) == 0
