@@ -36,7 +36,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_tree_amd", "csrc", f)
                   for f in KERNEL_SOURCE_NAMES]
 # the bf16 verify kernel with preparation inside, which the default step
 # launches (name as rocprofv3 prints it)
-DOMINANT_KERNEL = "verify_kernel<1, true, true, true>"
+DOMINANT_KERNEL = "verify_kernel<1, true, true, true, 0>"
 
 
 def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
@@ -93,6 +93,37 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     return name.split("(")[0].replace("void ", "")
+
+
+def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
+    """Scaled HBM bytes per dispatch of every library kernel in the two counter
+    passes, beside the algorithmic bytes where a model exists (target shape)."""
+    def means(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] == counter and "bole::" in r["Kernel_Name"]:
+                acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+    fe, wr = means(fetch_dir, "FETCH_SIZE"), means(write_dir, "WRITE_SIZE")
+    cfg = W.CONFIGS["target"]
+    forests = [W.make_forest(cfg, seed) for seed in range(4)]
+    algo = {
+        "bole::verify_kernel<1, true, true, true, 0>": np.mean(
+            [tree_verify_algorithmic_bytes(f.sizes(), cfg.H, cfg.d_k, cfg.d_v, 2) for f in forests]),
+        "bole::commit_kernel<1>": np.mean(
+            [commit_algorithmic_bytes(f, 1, cfg.H, cfg.d_k, cfg.d_v, 2) for f in forests]),
+        "bole::tree_conv_kernel<1>": conv_algorithmic_bytes(
+            forests[0].N, cfg.B, W.conv_channels(cfg), W.CONV_WIDTH, 2),
+    }
+    out = ["## Every library kernel in the same two passes", "",
+           "| kernel | dispatches | FETCH KiB | WRITE KiB | HBM MB (scaled) | algorithmic MB | ratio |",
+           "|---|---|---|---|---|---|---|"]
+    for k in sorted(set(fe) & set(wr)):
+        hbm = (fe[k][0] * f_fetch + wr[k][0] * f_write) * 1024.0
+        a = algo.get(k)
+        out.append(f"| `{k}` | {fe[k][1]} | {fe[k][0]:.0f} | {wr[k][0]:.0f} | {hbm / 1e6:.1f} | "
+                   + (f"{a / 1e6:.1f} | {hbm / a:.3f} |" if a else "| |"))
+    return out
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
@@ -152,7 +183,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
           f"| algorithmic bytes per launch | {algo / 1e6:.1f} MB |",
           f"| ratio | {traffic / algo:.3f} |", "",
           f"Kernel source hash: `{rec['kernel_source_hash']}` ({', '.join(KERNEL_SOURCE_NAMES)}); "
-          "bench.py reports `traffic` only while it matches."]
+          "bench.py reports `traffic` only while it matches.", ""]
+    md += all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write)
     with open(os.path.join(PROFILES, "bole_tree_verify_target_counters.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(rec))
