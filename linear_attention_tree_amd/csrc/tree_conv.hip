@@ -28,7 +28,11 @@ struct ConvCfg {
   static constexpr int EPP = 16 / sizeof(Elem);              // elements per 16-byte piece
   static constexpr int CH = DT == BOLE_BF16 ? 256 : 128;      // channels per workgroup (512 B)
   static constexpr int GROUPS = CH / EPP;                    // pieces per row
-  static constexpr int NODE_LANES = kConvThreads / GROUPS;   // nodes computed at once
+  static constexpr int NQ = 2;                               // parts taken in turn
+  static constexpr int HG = GROUPS / NQ;                     // pieces per row and part
+  static constexpr int NODE_LANES = kConvThreads / HG;       // nodes computed at once
+  // 16-byte pieces per thread and part: tree rows plus committed state rows
+  static constexpr int PIECES = (kMaxTree + kMaxConv - 1) * HG / kConvThreads + 1;
 };
 
 __device__ __forceinline__ float elem_to_float(uint16_t b) { return bf16_bits_to_float(b); }
@@ -38,6 +42,13 @@ __device__ __forceinline__ float elem_to_float(float f) { return f; }
 // for the workgroup's channels, rows kMaxTree .. kMaxTree + W - 2 the committed
 // conv state.  src[i][j] is the tile row of the j-th most recent entry of node
 // i's window (j = 0: node i itself).
+//
+// The workgroup's channels are taken in NQ parts.  A part's loads go out once
+// the part before it has arrived, and the part before it is then computed and
+// stored while they are in flight: the output writes of one part overlap the
+// input reads of the next.  (Issued all at once, every part would arrive only
+// near the end of the whole transfer: the memory system serves the requests
+// of all workgroups interleaved.)
 template <int DT>
 __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
     const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
@@ -70,26 +81,32 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
   const Elem* xe = reinterpret_cast<const Elem*>(x);
   const Elem* se = reinterpret_cast<const Elem*>(conv_state);
 
-  // Every load goes out before any is waited on: wave 0's parent links first
-  // (the topology below waits only for them), then each thread's pieces of
-  // the tree's input rows and the committed state rows, then the weights.  A
-  // piece past the rows needed or past C reads piece 0 of row 0 and is not
-  // stored.
+  // Wave 0's parent links go out first (the topology below waits only for
+  // them), then each thread's pieces of part 0 of the tree's input rows and of
+  // the committed state rows, then the taps.  A piece past the rows needed or
+  // past C reads piece 0 of row 0 and is not stored.
   int p = -1;
   if (w == 0) p = parent[off + min(lane, T - 1)];
-  constexpr int kPieces = (kMaxTree + kMaxConv - 1) * CC::GROUPS / kConvThreads + 1;
-  const int n_pieces = (T + Wd - 1) * CC::GROUPS;
-  u16x8 buf[kPieces];
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
+  const int n_pieces = (T + Wd - 1) * CC::HG;
+  auto piece = [&](int h, int k, int& r, int& col) {  // tile row and column of a piece
     const int id = threadIdx.x + kConvThreads * k;
-    const int r = id / CC::GROUPS, pc = id - (id / CC::GROUPS) * CC::GROUPS;
-    const int c = c0 + CC::EPP * pc;
-    const bool use = id < n_pieces && c < C;
-    const Elem* row = !use ? xe : r < T ? xe + (int64_t)(off + r) * C
-                                        : se + ((int64_t)s * (Wd - 1) + (r - T)) * C;
-    buf[k] = *reinterpret_cast<const u16x8*>(row + (use ? c : 0));
-  }
+    r = id / CC::HG;
+    col = CC::EPP * (CC::HG * h + (id - (id / CC::HG) * CC::HG));
+    return id < n_pieces && c0 + col < C;
+  };
+  u16x8 buf[CC::NQ][CC::PIECES];
+  auto issue = [&](auto h_tag) {
+    constexpr int h = decltype(h_tag)::value;
+#pragma unroll
+    for (int k = 0; k < CC::PIECES; ++k) {
+      int r, col;
+      const bool use = piece(h, k, r, col);
+      const Elem* row = !use ? xe : r < T ? xe + (int64_t)(off + r) * C
+                                          : se + ((int64_t)s * (Wd - 1) + (r - T)) * C;
+      buf[h][k] = *reinterpret_cast<const u16x8*>(row + (use ? c0 + col : 0));
+    }
+  };
+  issue(std::integral_constant<int, 0>{});
   constexpr int kWPer = kMaxConv * CC::CH / kConvThreads;
   float wv[kWPer];
 #pragma unroll
@@ -121,28 +138,32 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
       if (tp.fail && reporter) report(err, tp.fail);
     }
   }
+  auto park = [&](auto h_tag) {  // waits for part h's pieces
+    constexpr int h = decltype(h_tag)::value;
 #pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
-    const int id = threadIdx.x + kConvThreads * k;
-    const int r = id / CC::GROUPS, pc = id - (id / CC::GROUPS) * CC::GROUPS;
-    if (id < n_pieces && c0 + CC::EPP * pc < C)
-      *reinterpret_cast<u16x8*>(&tile[r < T ? r : kMaxTree + r - T][CC::EPP * pc]) = buf[k];
-  }
+    for (int k = 0; k < CC::PIECES; ++k) {
+      int r, col;
+      if (piece(h, k, r, col))
+        *reinterpret_cast<u16x8*>(&tile[r < T ? r : kMaxTree + r - T][col]) = buf[h][k];
+    }
+  };
+  park(std::integral_constant<int, 0>{});
 #pragma unroll
   for (int k = 0; k < kWPer; ++k) {
     const int id = threadIdx.x + kConvThreads * k;
     ws[id / CC::CH][id - (id / CC::CH) * CC::CH] = wv[k];
   }
   if (threadIdx.x < CC::CH) bs[threadIdx.x] = c0 + (int)threadIdx.x < C ? bv : 0.0f;
-  __syncthreads();
-  if (!tree_ok) return;
+  __syncthreads();  // part 0, taps, bias and the window table visible
+  if (!tree_ok) return;  // uniform
 
-  const int pc = threadIdx.x % CC::GROUPS, nl = threadIdx.x / CC::GROUPS;
-  const int cl = CC::EPP * pc, c = c0 + cl;
-  if (c >= C) return;  // no barrier follows
-  Elem* ye = reinterpret_cast<Elem*>(y) + c;
-  auto nodes = [&](auto wd_tag) {
+  const int pc = threadIdx.x % CC::HG, nl = threadIdx.x / CC::HG;
+  auto half = [&](auto h_tag, auto wd_tag) {
+    constexpr int h = decltype(h_tag)::value;
     constexpr int WD = decltype(wd_tag)::value;
+    const int cl = CC::EPP * (CC::HG * h + pc), c = c0 + cl;
+    if (c >= C) return;
+    Elem* ye = reinterpret_cast<Elem*>(y) + c;
     // the thread's taps and bias stay in registers across its nodes
     float wr[WD][CC::EPP], br[CC::EPP];
 #pragma unroll
@@ -180,16 +201,32 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
       __builtin_nontemporal_store(out, reinterpret_cast<u16x8*>(ye + (int64_t)(off + i) * C));
     }
   };
-  switch (Wd) {
-    case 1: nodes(std::integral_constant<int, 1>{}); break;
-    case 2: nodes(std::integral_constant<int, 2>{}); break;
-    case 3: nodes(std::integral_constant<int, 3>{}); break;
-    case 4: nodes(std::integral_constant<int, 4>{}); break;
-    case 5: nodes(std::integral_constant<int, 5>{}); break;
-    case 6: nodes(std::integral_constant<int, 6>{}); break;
-    case 7: nodes(std::integral_constant<int, 7>{}); break;
-    default: nodes(std::integral_constant<int, 8>{}); break;
-  }
+  auto compute = [&](auto h_tag) {  // the width as a compile-time constant
+    switch (Wd) {
+      case 1: half(h_tag, std::integral_constant<int, 1>{}); break;
+      case 2: half(h_tag, std::integral_constant<int, 2>{}); break;
+      case 3: half(h_tag, std::integral_constant<int, 3>{}); break;
+      case 4: half(h_tag, std::integral_constant<int, 4>{}); break;
+      case 5: half(h_tag, std::integral_constant<int, 5>{}); break;
+      case 6: half(h_tag, std::integral_constant<int, 6>{}); break;
+      case 7: half(h_tag, std::integral_constant<int, 7>{}); break;
+      default: half(h_tag, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  auto stage = [&](auto h_tag, auto self) {
+    constexpr int h = decltype(h_tag)::value;
+    if constexpr (h + 1 < CC::NQ) {
+      issue(std::integral_constant<int, h + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(h_tag);
+    if constexpr (h + 1 < CC::NQ) {
+      park(std::integral_constant<int, h + 1>{});
+      __syncthreads();  // part h + 1 visible (other parts' columns are not touched)
+      self(std::integral_constant<int, h + 1>{}, self);
+    }
+  };
+  stage(std::integral_constant<int, 0>{}, stage);
 }
 
 // grid (B, ceil(C / 256)); thread = channel.  Reads every source of the new
