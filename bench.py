@@ -479,6 +479,42 @@ def build_states_device(cfg, B, layer, seed, torch, TreeRound, dev):
     return pool
 
 
+def time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K):
+    """Whole rounds from drafted candidates: budget selection and packing, the
+    L per-layer tree_verify launches and one commit, captured once per capacity
+    bucket (BucketedRound) and timed as graph replays.  Token operands are the
+    round's device-drawn layers; each tree accepts its last packed node."""
+    from linear_attention_tree_amd import BucketedRound
+    B, L, N = cfg.B, cfg.L, x.q.shape[1]
+    cands = W.make_candidates(B, seed=5)
+    buckets = [N // 2, N]
+    br = BucketedRound(B, L, cfg.H, cfg.d_k, cfg.d_v, x.v.dtype, int(cands.cand_off[-1]), buckets,
+                       device=dev)
+    for name in ("q", "k", "v", "g", "beta"):
+        getattr(br, name).copy_(getattr(x, name))
+    br.cand_parent.copy_(torch.from_numpy(cands.cand_parent))
+    br.p_draft.copy_(torch.from_numpy(cands.p_draft))
+    br.cand_off.copy_(torch.from_numpy(cands.cand_off))
+    pool_b = pool.clone()
+    sizes = {}
+    for c in buckets:  # each bucket's forest, for its accepted nodes
+        br.forest[c].build(br.cand_parent, br.p_draft, br.cand_off)
+        sizes[c] = np.diff(br.forest[c].tree_off.cpu().numpy())
+    br.accept.zero_()  # the roots: valid in every bucket's forest for the capture passes
+    br.capture(pool_b, slot)
+    out = {}
+    for c in buckets:
+        br.accept.copy_(torch.from_numpy((sizes[c] - 1).astype(np.int32)))
+        ms = time_graphs([br.graphs[c]], max(K // 4, 5), torch)
+        out[str(c)] = {"ms_per_round": ms, "nodes": int(sizes[c].sum()),
+                       "node_heads_per_s": float(sizes[c].sum()) * cfg.H * L / (ms * 1e-3)}
+    assert int(br.err.item()) == 0, "device error bits set"
+    return {"note": "per capacity bucket: bole_forest_build over drafted candidates "
+                    f"({int(cands.cand_off[-1])} for {B} requests), {L} x bole_tree_verify, one "
+                    "bole_commit_path; one captured graph per bucket",
+            "by_capacity": out}
+
+
 def round_main(cfg, args, torch, TreeRound, bole, dev):
     """One step = one verification round over cfg.L layers: the per-layer
     verify launches, then one commit over all layers (in place, so each round
@@ -540,6 +576,7 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
     cbytes = commit_algorithmic_bytes(f, L, H, cfg.d_k, cfg.d_v, e)
     ms_layer = ms_verify / L
     step = ms_round[args.path]
+    buckets = time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K)
     achieved = vbytes / (ms_layer * 1e-3) / 1e9
     c_achieved = cbytes / (ms_commit * 1e-3) / 1e9
     out = {
@@ -570,6 +607,7 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
                                    "split: one workspace reused by every layer":
                                    int(bole.bole_gc_workspace_bytes(B, H))},
             "transient_bytes_per_round": {"U + logP": L * N * H * (4 * cfg.d_v + 4)},
+            "bucketed_rounds": buckets,
         },
         "roofline": {
             "kernel": "bole_" + dominant,

@@ -13,12 +13,12 @@ from .bole import (  # noqa: F401
     bole_tree_verify, bole_verify, bole_verify_neumann, bole_factor_inverse, bole_verify_inverse,
     bole_forest_build, bole_forest_workspace_bytes, lib,
 )
-from .runner import ForestBuilder, Topology, TreeRound  # noqa: F401
+from .runner import BucketedRound, ForestBuilder, Topology, TreeRound  # noqa: F401
 
 __all__ = [
     "bole_tree_prep", "bole_factor_gc", "bole_verify", "bole_factor_verify", "bole_tree_verify",
     "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
     "bole_commit_path", "bole_tree_conv", "bole_conv_commit", "bole_forest_build",
-    "bole_forest_workspace_bytes", "ForestBuilder",
+    "bole_forest_workspace_bytes", "ForestBuilder", "BucketedRound",
     "bole_gc_workspace_bytes", "bole_status_string", "BoleError", "TreeRound", "Topology", "lib",
 ]

@@ -159,3 +159,95 @@ class ForestBuilder:
                                self.rho, self.parent, self.cand_of, self.tree_off,
                                self.workspace, self.err, stream)
         return self.parent, self.tree_off, self.cand_of
+
+
+def capture_graph(fn):
+    """A HIP graph of the launches fn() makes on the current stream (one
+    uncaptured pass first, on the side stream torch captures on)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+class BucketedRound:
+    """A whole verification round as one captured HIP graph per capacity
+    bucket: budget selection and forest packing (bole_forest_build), each
+    layer's bole_tree_verify, then one bole_commit_path over all layers.
+
+    Every buffer the graphs touch keeps its address: a round copies its
+    drafted candidates, its token operands (packed-forest order, the first
+    `capacity` rows of each layer) and its accepted nodes into the input
+    buffers and replays the graph of the smallest bucket whose capacity holds
+    its budget.  The verify grid does not depend on the node count, so one
+    bucket's graph serves every forest up to its capacity."""
+
+    def __init__(self, B: int, L: int, H: int, d_k: int, d_v: int, dtype: torch.dtype,
+                 M_total: int, buckets, max_tree: int = bole.MAX_TREE, device="cuda"):
+        dev = torch.device(device)
+        i32, f32 = torch.int32, torch.float32
+        self.B, self.L, self.H = B, L, H
+        self.buckets = sorted(int(c) for c in buckets)
+        cmax = self.buckets[-1]
+        self.cand_parent = torch.zeros(M_total, dtype=i32, device=dev)
+        self.p_draft = torch.zeros(M_total, dtype=f32, device=dev)
+        self.cand_off = torch.zeros(B + 1, dtype=i32, device=dev)
+        self.q = torch.zeros(L, cmax, H, d_k, dtype=dtype, device=dev)
+        self.k = torch.zeros_like(self.q)
+        self.v = torch.zeros(L, cmax, H, d_v, dtype=dtype, device=dev)
+        self.g = torch.zeros(L, cmax, H, dtype=f32, device=dev)
+        self.beta = torch.zeros(L, cmax, H, dtype=f32, device=dev)
+        self.accept = torch.zeros(B, dtype=i32, device=dev)
+        self.O = torch.zeros(L, cmax, H, d_v, dtype=dtype, device=dev)
+        self.U = torch.zeros(L, cmax, H, d_v, dtype=f32, device=dev)
+        self.logP = torch.zeros(L, cmax, H, dtype=f32, device=dev)
+        self.err = torch.zeros(1, dtype=i32, device=dev)
+        self.forest = {c: ForestBuilder(B, M_total, c, max_tree, dev, self.err)
+                       for c in self.buckets}
+        self.topo = {c: Topology(parent=self.forest[c].parent, tree_off=self.forest[c].tree_off,
+                                 depth=torch.zeros(c, dtype=i32, device=dev),
+                                 anc=torch.zeros(c, dtype=torch.int64, device=dev),
+                                 order=torch.zeros(c, dtype=i32, device=dev),
+                                 tree_depth=torch.zeros(B, dtype=i32, device=dev))
+                     for c in self.buckets}
+        self.graphs = {}
+
+    def bucket(self, budget: int) -> int:
+        for c in self.buckets:
+            if budget <= c:
+                return c
+        raise ValueError(f"budget {budget} exceeds the largest bucket {self.buckets[-1]}")
+
+    def run_eager(self, capacity: int, state_pool, slot, commit=True):
+        """One round launched call by call (what the graph of `capacity` holds)."""
+        fb, t, c = self.forest[capacity], self.topo[capacity], capacity
+        fb.build(self.cand_parent, self.p_draft, self.cand_off)
+        for l in range(self.L):
+            bole.bole_tree_verify(self.q[l, :c], self.k[l, :c], self.v[l, :c], fb.parent,
+                                  self.g[l, :c], self.beta[l, :c], state_pool[l], slot,
+                                  fb.tree_off, self.O[l, :c], self.U[l, :c], t.depth, t.anc,
+                                  t.order, t.tree_depth, self.logP[l, :c], self.err)
+        if commit:
+            bole.bole_commit_path(state_pool, slot, self.k[:, :c], self.U[:, :c],
+                                  self.logP[:, :c], t.anc, fb.tree_off, self.accept, self.err)
+
+    def capture(self, state_pool, slot, commit=True):
+        """Capture every bucket's round against these state-pool and slot
+        buffers (they too must keep their addresses).  The uncaptured pass that
+        precedes each capture runs the round once, commit included, on the
+        inputs loaded now: load a valid round first (empty candidate sets give
+        empty trees, which the verify calls report)."""
+        for c in self.buckets:
+            self.graphs[c] = capture_graph(
+                lambda c_=c: self.run_eager(c_, state_pool, slot, commit))
+
+    def replay(self, budget: int) -> int:
+        c = self.bucket(budget)
+        self.graphs[c].replay()
+        return c
