@@ -24,7 +24,12 @@
 //  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
 //           a permuted K order (load_tri_blocks) that makes the lane's own U
 //           tiles the B operand: U never leaves registers.
-//  Readout  O = B0 + C U, float32 accumulation.
+//  Readout  O = B0 + C U, float32 accumulation.  Products that U and the
+//           committed state depend on split every float32 operand hi + lo; O's
+//           own (Q S_pre, C U) do so only for float32 tokens (kOExact).
+//  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
+//           leave as 4-element pieces of the nodes' rows; V arrives the same
+//           way, as 16-byte row pieces staged for the accumulator layout.
 //
 // Two other exact solves can be selected (SOLVE):
 //  Neumann  the d_b-step propagation of Eq. 8 as the pages run it: Z <- -G Z,
@@ -33,12 +38,7 @@
 //           above m and input tiles whose deepest row is above m - 1.
 //  Inverse  the G and C inputs hold W = (I + G)^-1 and M = C W (formed by
 //           bole_factor_inverse): U = W R and O = B0 + M R, two independent
-//           products with no chain between tiles.  Products that U and the
-//           committed state depend on split every float32 operand hi + lo; O's
-//           own (Q S_pre, C U) do so only for float32 tokens (kOExact).
-//  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
-//           leave as 4-element pieces of the nodes' rows; V arrives the same
-//           way, as 16-byte row pieces staged for the accumulator layout.
+//           products with no chain between tiles.
 #include <type_traits>
 
 #include "tree_topo.h"
