@@ -76,8 +76,9 @@ typedef enum {
 
 /*
  * bole_tree_prep - round-level topology step plus log-space gate products
- * (arXiv page: "one round-level topology step followed by three per-layer GPU
- * stages"; review section 三, fused pipeline, stage (1) gate preparation).
+ * (arXiv page, section IV-C: a topology step once per round precedes the
+ * per-layer GPU stages; review section 三, fused pipeline, stage (1) gate
+ * preparation).
  *
  *  in   parent[N]           local parent index per node (-1 = root)
  *  in   tree_off[B+1]       tree row ranges
