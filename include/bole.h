@@ -269,9 +269,9 @@ BOLE_API int bole_tree_verify(int32_t dtype, const void* q, const void* k, const
 
 /*
  * bole_tree_conv - tree-parallel short causal convolution, the first per-layer
- * stage of the fused tree pipeline (arXiv page, sections II-A and IV-C; review
- * page, fused-pipeline paragraph: each node fuses convolution, bias and SiLU
- * along its parent links, all nodes at once).
+ * stage of the fused tree pipeline, with the bias and SiLU applied in the same
+ * pass (arXiv page, sections II-A and IV-C; review page, fused-pipeline
+ * paragraph).
  *
  * Node i's window is the last W entries of its request's committed conv state
  * (the W - 1 inputs that preceded the tree, oldest first) followed by the

@@ -1,7 +1,8 @@
 // Tree-parallel short causal convolution: the first per-layer stage of the
 // fused tree pipeline (arXiv page of Bole, section IV-C; review page, fused
-// pipeline paragraph: every node fuses convolution, bias and SiLU along its
-// parent links, all nodes at once).  The GDN layer's depthwise causal
+// pipeline paragraph).  Each node's window is gathered by following its
+// parents; the taps, the bias and SiLU are applied in the same pass, and the
+// nodes are independent of one another.  The GDN layer's depthwise causal
 // convolution (arXiv page, section II-A) sees, at node i, the last W entries of
 // the request's committed conv state (the W - 1 inputs that preceded the tree,
 // oldest first) followed by the inputs along i's root-to-node path: exactly

@@ -6,10 +6,10 @@ numpy, one node at a time.
 
 A GDN layer passes its mixed projections through a short causal depthwise
 convolution before the recurrence (arXiv page of Bole, section II-A).  The
-fused tree pipeline runs it tree-parallel as its first per-layer stage: each
-node fuses convolution, bias and SiLU along its parent links, all nodes at
-once (review page, fused-pipeline paragraph; arXiv page, section IV-C).  The
-pages give no kernel width, so it is a parameter W.
+fused tree pipeline runs it as its first per-layer stage, tree-parallel, with
+the bias and SiLU in the same pass; a node's inputs come from its ancestors
+(review page, fused-pipeline paragraph; arXiv page, section IV-C).  The pages
+give no kernel width, so it is a parameter W.
 
 Reading (stated, since the pages leave it open): node i's window is the last W
 entries of the sequence formed by the request's committed conv state (the
