@@ -142,3 +142,18 @@ def test_tree_conv_rejected_tree(bad, bits):
                            ci.state64, np.array([0, 2], np.int32))
     yk = y.float().cpu().numpy().astype(np.float64)[keep]
     assert tree_err(yk, ref, fg.tree_off) <= 2e-2
+
+
+def test_tree_conv_target_shape():
+    """The benchmarked launch: the target forest (16 trees x 64 nodes), the mixed
+    q/k/v projection's 12288 channels, width 4, bf16; every output against the
+    oracle, and the commit bit for bit."""
+    cfg = W.CONFIGS["target"]
+    forest = W.make_forest(cfg, seed=0)
+    C = W.conv_channels(cfg)
+    say(f"tree conv target shape: N={forest.N} C={C} W={W.CONV_WIDTH}")
+    out = run(cfg, forest, C, W.CONV_WIDTH)
+    e = tree_err(out["y"], out["ref"], forest.tree_off)
+    say(f"  y {e:.2e} (bar 0.02)")
+    assert out["err"] == 0 and e <= 2e-2
+    assert np.array_equal(out["st"], out["ref_st"])
