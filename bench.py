@@ -126,6 +126,41 @@ def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
     return out
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def summarize_mfma(mfma_dir, trace_dir, command):
+    """MFMA and LDS counters of every library kernel (one rocprofv3 --pmc pass
+    of this script) against the kernel-trace durations."""
+    acc = {}
+    for r in _csv_rows(mfma_dir, "counter_collection.csv"):
+        if "bole::" in r["Kernel_Name"] and r["Counter_Name"] in MFMA_COUNTERS:
+            acc.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    dur = {_short(r["Name"]): float(r["AverageNs"]) for r in _csv_rows(trace_dir, "kernel_stats.csv")}
+    lines = ["# MFMA and LDS counters, target workload (rocprofv3 --pmc)", "", "Command:", "", "```",
+             command, "```", "",
+             "Per dispatch, averaged over the run. bf16 MFMA rate = 512 x "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 / the kernel's average duration in the kernel trace, "
+             f"against the {PEAK_BF16_TFLOPS:.0f} TFLOP/s dense bf16 peak. LDS bank-conflict share = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | bf16 MFMA TFLOP/s | of peak | LDS instructions | "
+             "LDS bank-conflict share |", "|---|---|---|---|---|"]
+    for k in sorted(acc):
+        c = {n: sum(v) / len(v) for n, v in acc[k].items()}
+        if len(c) < len(MFMA_COUNTERS) or k not in dur:
+            continue
+        tflops = 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / (dur[k] * 1e-9) / 1e12
+        conf = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
+        lines.append(f"| `{k}` | {tflops:.1f} | {tflops / PEAK_BF16_TFLOPS:.3f} | "
+                     f"{c['SQ_INSTS_LDS']:.0f} | {conf:.3f} |")
+    with open(os.path.join(PROFILES, "bole_kernels_target_mfma_lds.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     """Turn three rocprofv3 runs of this script (a kernel trace, a FETCH_SIZE
     pass and a WRITE_SIZE pass, the counter passes preceded by a plain copy of
@@ -425,6 +460,34 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     return ms, nbytes
 
 
+def copy_bandwidth(torch, dev, footprint_bytes, reps):
+    """GB/s of a plain device copy (read + write) whose source and destination
+    together span footprint_bytes, timed as graph replays."""
+    n = footprint_bytes // 8
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    g = capture(torch, lambda: dst.copy_(src))
+    ms = time_graphs([g], reps, torch)
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def time_depth16(cfg, torch, TreeRound, bole, dev, reps):
+    """Sensitivity: bole_tree_verify on the workload's shape with trees drawn
+    under a depth cap of 16 instead of cfg.D (ms per launch, algorithmic bytes)."""
+    from dataclasses import replace
+    c16 = replace(cfg, D=16)
+    sets = [InputSet(c16, seed, torch, TreeRound, dev) for seed in range(2)]
+    for s_ in sets:
+        run_step(s_, bole, "tree")
+    n_in = 16
+    g = capture(torch, lambda: [launch(sets[i % 2], bole, "tree_verify") for i in range(n_in)])
+    ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
+    depth = max(int(s_.rnd.topo.tree_depth.max().item()) for s_ in sets)
+    nb = np.mean([tree_verify_algorithmic_bytes(s_.sizes, cfg.H, cfg.d_k, cfg.d_v,
+                                                2 if cfg.dtype == "bf16" else 4) for s_ in sets])
+    return ms, nb, depth
+
+
 def time_forest_build(cfg, torch, ForestBuilder, dev, reps, capacity):
     """Budget selection and packing for the workload's requests: drafted
     candidate trees (depth 8, top-k 4) of cfg.B requests, the given forest
@@ -649,12 +712,17 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "TRACE_DIR"),
+                    help="write the MFMA/LDS counter summary under profiles/ and exit")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from three rocprofv3 runs of this script "
                          "(no GPU needed)")
     ap.add_argument("--profile-commands", default="",
                     help="JSON {trace, fetch, write} of the commands that made the runs")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.profile_commands or "?")
+        return
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.calibrate_copy_mib or 256,
                            json.loads(args.profile_commands or "{}") or
@@ -736,6 +804,7 @@ def main():
                                               for i in range(n_in)])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     conv_ms, conv_bytes = time_tree_conv(cfg, sets, torch, bole, dev, K)
+    d16_ms, d16_bytes, d16_depth = time_depth16(cfg, torch, TreeRound, bole, dev, K)
     from linear_attention_tree_amd import ForestBuilder
     forest_runs = {}
     for cap in (cfg.B * cfg.T, 768):
@@ -749,6 +818,8 @@ def main():
     value = nodes * cfg.H / (ms_step * 1e-3)
     vbytes = np.mean([bytes_fn(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
     achieved = vbytes / (avg[dominant] * 1e-3) / 1e9
+    # a plain copy over the same footprint as the rotated input sets
+    copy_gbs = copy_bandwidth(torch, dev, int(vbytes * len(sets)), 20)
     # the committed counter record is the default path's dominant kernel
     traffic = traffic_from_profile(kernel_source_hash()) if args.path == "tree" else None
 
@@ -775,6 +846,12 @@ def main():
             "ms_per_step_other_path": ms_other,
             "ms_per_step_eager_launches": ms_eager,
             "kernel_ms_back_to_back": avg,
+            "tree_verify_depth_cap_16": {
+                "note": "sensitivity: the same shape with trees drawn under a depth cap of 16",
+                "ms": d16_ms, "deepest_tree": d16_depth,
+                "achieved_GBs": d16_bytes / (d16_ms * 1e-3) / 1e9,
+                "frac_of_hbm_peak": d16_bytes / (d16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            },
             "stage1_tree_conv": {
                 "note": "first pipeline stage (short causal conv + bias + SiLU along parent "
                         "links), not part of the step",
@@ -799,6 +876,8 @@ def main():
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": vbytes,
+            "copy_GBs": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
         },
     }
     if not args.no_cpu_baseline:
