@@ -126,36 +126,39 @@ def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
     return out
 
 
-MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_INSTS_LDS", "TCC_HIT_sum", "TCC_MISS_sum")
 PEAK_BF16_TFLOPS = 2500.0
 
 
 def summarize_mfma(mfma_dir, trace_dir, command):
-    """MFMA and LDS counters of every library kernel (one rocprofv3 --pmc pass
-    of this script) against the kernel-trace durations."""
+    """MFMA, LDS and L2 counters of every library kernel (one rocprofv3 --pmc
+    pass of this script) against the kernel-trace durations."""
     acc = {}
     for r in _csv_rows(mfma_dir, "counter_collection.csv"):
         if "bole::" in r["Kernel_Name"] and r["Counter_Name"] in MFMA_COUNTERS:
             acc.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
     dur = {_short(r["Name"]): float(r["AverageNs"]) for r in _csv_rows(trace_dir, "kernel_stats.csv")}
-    lines = ["# MFMA and LDS counters, target workload (rocprofv3 --pmc)", "", "Command:", "", "```",
+    lines = ["# MFMA, LDS and L2 counters, target workload (rocprofv3 --pmc)", "", "Command:", "", "```",
              command, "```", "",
              "Per dispatch, averaged over the run. bf16 MFMA rate = 512 x "
              "SQ_INSTS_VALU_MFMA_MOPS_BF16 / the kernel's average duration in the kernel trace, "
              f"against the {PEAK_BF16_TFLOPS:.0f} TFLOP/s dense bf16 peak. LDS bank-conflict share = "
-             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + "
+             "TCC_MISS_sum); the two-call verify (`verify_kernel<1, false, ...>`) reads G and C right "
+             "after the producer wrote them.", "",
              "| kernel | bf16 MFMA TFLOP/s | of peak | LDS instructions | "
-             "LDS bank-conflict share |", "|---|---|---|---|---|"]
+             "LDS bank-conflict share | L2 hit rate |", "|---|---|---|---|---|---|"]
     for k in sorted(acc):
         c = {n: sum(v) / len(v) for n, v in acc[k].items()}
         if len(c) < len(MFMA_COUNTERS) or k not in dur:
             continue
         tflops = 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / (dur[k] * 1e-9) / 1e12
         conf = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
+        hit = c["TCC_HIT_sum"] / max(c["TCC_HIT_sum"] + c["TCC_MISS_sum"], 1.0)
         lines.append(f"| `{k}` | {tflops:.1f} | {tflops / PEAK_BF16_TFLOPS:.3f} | "
-                     f"{c['SQ_INSTS_LDS']:.0f} | {conf:.3f} |")
+                     f"{c['SQ_INSTS_LDS']:.0f} | {conf:.3f} | {hit:.3f} |")
     with open(os.path.join(PROFILES, "bole_kernels_target_mfma_lds.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
