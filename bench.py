@@ -446,7 +446,7 @@ def conv_algorithmic_bytes(N, B, C, Wd, e):
 def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     """The first-stage tree convolution at the workload's shape: C = H (2 d_k +
     d_v) channels (the mixed q, k, v projection), width W.CONV_WIDTH.  Returns
-    (ms per launch, algorithmic bytes per launch)."""
+    (ms per launch, algorithmic bytes per launch, ms per conv-state commit)."""
     C, Wd = W.conv_channels(cfg), W.CONV_WIDTH
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     gen = torch.Generator(device=dev)
@@ -466,7 +466,12 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
     e = 2 if cfg.dtype == "bf16" else 4
     nbytes = np.mean([conv_algorithmic_bytes(s_.forest.N, s_.forest.B, C, Wd, e) for s_ in sets])
-    return ms, nbytes
+    # the conv-state commit of the accepted paths (moves W - 1 rows per request)
+    commits = [(r[3], r[4], r[0], r[5], r[6], s_.accept, r[8]) for r, s_ in zip(runs, sets)]
+    gc = capture(torch, lambda: [bole.bole_conv_commit(*commits[i % len(commits)])
+                                 for i in range(n_in)])
+    ms_commit = time_graphs([gc], max(reps // n_in, 5), torch) / n_in
+    return ms, nbytes, ms_commit
 
 
 def copy_bandwidth(torch, dev, footprint_bytes, reps):
@@ -812,7 +817,7 @@ def main():
         g = capture(torch, lambda w_=which: [launch(sets[i % len(sets)], bole, w_)
                                               for i in range(n_in)])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
-    conv_ms, conv_bytes = time_tree_conv(cfg, sets, torch, bole, dev, K)
+    conv_ms, conv_bytes, conv_commit_ms = time_tree_conv(cfg, sets, torch, bole, dev, K)
     d16_ms, d16_bytes, d16_depth = time_depth16(cfg, torch, TreeRound, bole, dev, K)
     from linear_attention_tree_amd import ForestBuilder
     forest_runs = {}
@@ -862,12 +867,13 @@ def main():
                 "frac_of_hbm_peak": d16_bytes / (d16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             },
             "stage1_tree_conv": {
-                "note": "first pipeline stage (short causal conv + bias + SiLU along parent "
-                        "links), not part of the step",
+                "note": "first pipeline stage: the short causal convolution over each node's "
+                        "ancestors, with bias and SiLU; not part of the step",
                 "channels": W.conv_channels(cfg), "width": W.CONV_WIDTH, "ms": conv_ms,
                 "achieved_GBs": conv_bytes / (conv_ms * 1e-3) / 1e9,
                 "frac_of_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "algorithmic_bytes_per_launch": conv_bytes,
+                "conv_commit_ms": conv_commit_ms,
             },
             "forest_build": {
                 "note": "budget selection by cumulative draft probability and forest packing "
