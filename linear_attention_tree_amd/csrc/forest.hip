@@ -53,7 +53,9 @@ __global__ __launch_bounds__(kScoreThreads) void forest_score_kernel(
   __shared__ float pl[kMaxCand];
   __shared__ int settled[kMaxCand];  // round (= depth) at which the node's rho was set, or -1
   __shared__ float rh[kMaxCand];
-  __shared__ uint64_t key[kMaxCand];
+  // 8 spare entries: the rank loop may read up to 7 keys past the last one
+  // (unconditionally, the values discarded), which then stay inside the array
+  __shared__ uint64_t key[kMaxCand + 8];
   __shared__ int rkl[kMaxCand];
   __shared__ uint32_t flags;
   __shared__ int progress[3];  // nodes settled per round, rotating
