@@ -268,6 +268,52 @@ BOLE_API int bole_tree_verify(int32_t dtype, const void* q, const void* k, const
                               uint32_t* err, void* stream);
 
 /*
+ * bole_commit_tree_verify - the previous round's accepted-path commit of this
+ * layer (bole_commit_path's update, Eq. 10 of the paper) followed by
+ * bole_tree_verify of this round, in one launch.  In a serving loop a layer's
+ * commit only has to land before that layer's next verify, so it is deferred
+ * to it: each (tree, head) workgroup reads its slot state once, applies the
+ * previous round's path update in registers, writes the committed state back
+ * and verifies the new tree against it.  The state pool is read and written
+ * once per round instead of three times (verify read, commit read and write).
+ *
+ * Request b of this round is request b of the previous round, in the same
+ * slot[b].  The committed state equals bole_commit_path's bit for bit (the
+ * same MFMA steps on the same operands), so the outputs equal those of
+ * bole_commit_path followed by bole_tree_verify.
+ *
+ *  in     q, k, v, parent, log_gamma, beta, slot, tree_off, B, N, H, d_k, d_v
+ *                                 as bole_tree_verify (this round)
+ *  in/out state_pool[n_slots,H,d_v,d_k]  float32, committed in place
+ *  out    O, U, depth, anc, order, tree_depth, logP   as bole_tree_verify
+ *  in     prev_k[prev_N,H,d_k]    dtype, the previous round's keys of this layer
+ *                                 (8-byte aligned)
+ *  in     prev_U[prev_N,H,d_v]    float32, the previous round's U of this layer
+ *  in     prev_logP[prev_N,H]     float32, its gate sums of this layer
+ *  in     prev_anc[prev_N]        the previous forest's ancestor-or-self sets
+ *  in     prev_tree_off[B+1]      the previous forest's offsets
+ *  in     prev_accept[B]          accepted local node of the previous tree, or
+ *                                 -1: nothing to commit for request b
+ *  out    err                     as bole_tree_verify, plus TREE_SIZE and
+ *                                 BAD_ACCEPT for the previous round's data
+ * A rejected new tree still gets its request's commit; a rejected commit
+ * (bad previous range or accepted node) leaves the slot unchanged and the
+ * verify reads it as it is.  The previous round's buffers must not alias this
+ * round's outputs.  The d_k limit of bole_factor_verify applies.
+ */
+BOLE_API int bole_commit_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                                     const int32_t* parent, const float* log_gamma,
+                                     const float* beta, float* state_pool, int32_t n_slots,
+                                     const int32_t* slot, const int32_t* tree_off, int32_t B,
+                                     int32_t N, int32_t H, int32_t d_k, int32_t d_v, void* O,
+                                     float* U, int32_t* depth, uint64_t* anc, int32_t* order,
+                                     int32_t* tree_depth, float* logP, const void* prev_k,
+                                     const float* prev_U, const float* prev_logP,
+                                     const uint64_t* prev_anc, const int32_t* prev_tree_off,
+                                     const int32_t* prev_accept, int32_t prev_N, uint32_t* err,
+                                     void* stream);
+
+/*
  * bole_tree_conv - tree-parallel short causal convolution, the first per-layer
  * stage of the fused tree pipeline, with the bias and SiLU applied in the same
  * pass (arXiv page, sections II-A and IV-C; review page, fused-pipeline

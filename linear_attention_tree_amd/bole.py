@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.bole_tree_verify.restype = ctypes.c_int
         L.bole_tree_verify.argtypes = ([i32, P, P, P, P, P, P, P, i32, P, P]
                                        + [i32] * 5 + [P] * 9)
+        L.bole_commit_tree_verify.restype = ctypes.c_int
+        L.bole_commit_tree_verify.argtypes = ([i32, P, P, P, P, P, P, P, i32, P, P]
+                                              + [i32] * 5 + [P] * 13 + [i32, P, P])
         L.bole_tree_conv.restype = ctypes.c_int
         L.bole_tree_conv.argtypes = [i32, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, P, P, P]
         L.bole_conv_commit.restype = ctypes.c_int
@@ -344,6 +347,66 @@ def bole_tree_verify(q, k, v, parent, log_gamma, beta, state_pool, slot, tree_of
         _ptr(state_pool), state_pool.shape[0], _ptr(slot), _ptr(tree_off), B, N, H, d_k, d_v,
         _ptr(O), _ptr(U), _ptr(depth), _ptr(anc), _ptr(order), _ptr(tree_depth), _ptr(logP),
         _ptr(err), _stream(stream)))
+
+
+def bole_commit_tree_verify(q, k, v, parent, log_gamma, beta, state_pool, slot, tree_off, O, U,
+                            depth, anc, order, tree_depth, logP, prev_k, prev_U, prev_logP,
+                            prev_anc, prev_tree_off, prev_accept, err=None, stream=None):
+    """The previous round's path commit (prev_*) into the slots, then
+    bole_tree_verify of this round, in one launch; state_pool is updated in
+    place."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    B = tree_off.shape[0] - 1
+    if tuple(k.shape) != (N, H, d_k) or tuple(v.shape[:2]) != (N, H):
+        raise ValueError("q, k, v shapes disagree")
+    _need(parent, "parent", torch.int32, 1)
+    _need(tree_off, "tree_off", torch.int32, 1)
+    for t, nm in ((log_gamma, "log_gamma"), (beta, "beta"), (logP, "logP")):
+        _need(t, nm, torch.float32, 2)
+        if tuple(t.shape) != (N, H):
+            raise ValueError(f"{nm} must be [N, H]")
+    _need(state_pool, "state_pool", torch.float32, 4)
+    if tuple(state_pool.shape[1:]) != (H, d_v, d_k):
+        raise ValueError("state_pool must be [n_slots, H, d_v, d_k]")
+    _need(slot, "slot", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 1)
+    _need(order, "order", torch.int32, 1)
+    _need(depth, "depth", torch.int32, 1)
+    _need(tree_depth, "tree_depth", torch.int32, 1)
+    if parent.shape[0] != N or anc.shape[0] != N or order.shape[0] != N or depth.shape[0] != N:
+        raise ValueError("parent, anc, order and depth need N entries")
+    _need(O, "O", v.dtype, 3)
+    _need(U, "U", torch.float32, 3)
+    if tuple(O.shape) != (N, H, d_v) or tuple(U.shape) != (N, H, d_v):
+        raise ValueError("O and U must be [N, H, d_v]")
+    if slot.shape[0] != B or tree_depth.shape[0] != B:
+        raise ValueError("slot and tree_depth need B entries")
+    _need(prev_k, "prev_k", q.dtype, 3)
+    N0 = prev_k.shape[0]
+    if tuple(prev_k.shape) != (N0, H, d_k):
+        raise ValueError("prev_k must be [N0, H, d_k]")
+    _need(prev_U, "prev_U", torch.float32, 3)
+    if tuple(prev_U.shape) != (N0, H, d_v):
+        raise ValueError("prev_U must be [N0, H, d_v]")
+    _need(prev_logP, "prev_logP", torch.float32, 2)
+    if tuple(prev_logP.shape) != (N0, H):
+        raise ValueError("prev_logP must be [N0, H]")
+    _need(prev_anc, "prev_anc", torch.int64, 1)
+    _need(prev_tree_off, "prev_tree_off", torch.int32, 1)
+    _need(prev_accept, "prev_accept", torch.int32, 1)
+    if prev_anc.shape[0] != N0 or prev_tree_off.shape[0] != B + 1 or prev_accept.shape[0] != B:
+        raise ValueError("prev_anc needs N0 entries, prev_tree_off B+1, prev_accept B")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    _check("bole_commit_tree_verify", lib().bole_commit_tree_verify(
+        _code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(parent), _ptr(log_gamma), _ptr(beta),
+        _ptr(state_pool), state_pool.shape[0], _ptr(slot), _ptr(tree_off), B, N, H, d_k, d_v,
+        _ptr(O), _ptr(U), _ptr(depth), _ptr(anc), _ptr(order), _ptr(tree_depth), _ptr(logP),
+        _ptr(prev_k), _ptr(prev_U), _ptr(prev_logP), _ptr(prev_anc), _ptr(prev_tree_off),
+        _ptr(prev_accept), N0, _ptr(err), _stream(stream)))
 
 
 def bole_tree_conv(x, weight, bias, conv_state, slot, parent, tree_off, y, err=None,

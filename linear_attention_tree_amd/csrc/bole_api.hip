@@ -41,6 +41,13 @@ int bole_tree_verify_launch(int32_t, const void*, const void*, const void*, cons
                             const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, void*,
                             float*, int32_t*, uint64_t*, int32_t*, int32_t*, float*, uint32_t*,
                             hipStream_t);
+int bole_commit_tree_verify_launch(int32_t, const void*, const void*, const void*, const int32_t*,
+                                   const float*, const float*, float*, int32_t, const int32_t*,
+                                   const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t,
+                                   void*, float*, int32_t*, uint64_t*, int32_t*, int32_t*, float*,
+                                   const void*, const float*, const float*, const uint64_t*,
+                                   const int32_t*, const int32_t*, int32_t, uint32_t*,
+                                   hipStream_t);
 int bole_tree_conv_launch(int32_t, const void*, const float*, const float*, const void*, int32_t,
                           const int32_t*, const int32_t*, const int32_t*, int32_t, int32_t, int32_t,
                           int32_t, void*, uint32_t*, hipStream_t);
@@ -228,6 +235,31 @@ int bole_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
   return bole_tree_verify_launch(dtype, q, k, v, parent, log_gamma, beta, state_pool, n_slots,
                                  slot, tree_off, B, N, H, d_k, d_v, O, U, depth, anc, order,
                                  tree_depth, logP, err, (hipStream_t)stream);
+}
+
+int bole_commit_tree_verify(int32_t dtype, const void* q, const void* k, const void* v,
+                            const int32_t* parent, const float* log_gamma, const float* beta,
+                            float* state_pool, int32_t n_slots, const int32_t* slot,
+                            const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
+                            int32_t d_v, void* O, float* U, int32_t* depth, uint64_t* anc,
+                            int32_t* order, int32_t* tree_depth, float* logP, const void* prev_k,
+                            const float* prev_U, const float* prev_logP, const uint64_t* prev_anc,
+                            const int32_t* prev_tree_off, const int32_t* prev_accept,
+                            int32_t prev_N, uint32_t* err, void* stream) {
+  if (!dtype_ok(dtype)) return BOLE_E_DTYPE;
+  if (!q || !k || !v || !parent || !log_gamma || !beta || !state_pool || !slot || !tree_off ||
+      !O || !U || !depth || !anc || !order || !tree_depth || !logP || !prev_k || !prev_U ||
+      !prev_logP || !prev_anc || !prev_tree_off || !prev_accept)
+    return BOLE_E_NULL;
+  if (B < 1 || N < 1 || H < 1 || n_slots < 1 || prev_N < 1 || B > (1 << 24) || !grid_ok(B, H, 4))
+    return BOLE_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k > bole_factor_verify_max_dk(dtype) ||
+      (uintptr_t)prev_k % 8 != 0)
+    return BOLE_E_UNSUPPORTED;
+  return bole_commit_tree_verify_launch(
+      dtype, q, k, v, parent, log_gamma, beta, state_pool, n_slots, slot, tree_off, B, N, H, d_k,
+      d_v, O, U, depth, anc, order, tree_depth, logP, prev_k, prev_U, prev_logP, prev_anc,
+      prev_tree_off, prev_accept, prev_N, err, (hipStream_t)stream);
 }
 
 int bole_tree_conv(int32_t dtype, const void* x, const float* weight, const float* bias,

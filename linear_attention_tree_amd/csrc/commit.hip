@@ -19,8 +19,10 @@
 // A = k_j (bf16 exact; float32 keys split hi+lo), B = (P_a/P_j) U_j (float32,
 // split hi+lo).  The accumulator of a 16x16 tile holds four consecutive key
 // columns of one value row, which is one float4 of the slot: every slot
-// element is read once and written once, as P_a S + the path product in
-// float32.
+// element is read once and written once.  Each accumulator starts from P_a S
+// (one float32 product) and the path steps add onto it, so the deferred
+// commit inside bole_commit_tree_verify, which takes the same MFMA steps on the
+// same operands, produces the same bits.
 #include <type_traits>
 
 #include "common.h"
@@ -167,8 +169,16 @@ struct CommitWave {
   // stores are written through the L2 (device scope): the slot lines were just
   // read into it, and left dirty there they would all be written back after
   // the last wave (measured 1.6 us slower at the target shape).
-  __device__ __forceinline__ void store(int c0, const f32x4 (&sv)[kCommitTiles][kCommitTiles],
-                                        const f32x4 (&prod)[kCommitTiles][kCommitTiles]) const {
+  __device__ __forceinline__ void init(const f32x4 (&sv)[kCommitTiles][kCommitTiles],
+                                       f32x4 (&prod)[kCommitTiles][kCommitTiles]) const {
+#pragma unroll
+    for (int nt = 0; nt < kCommitTiles; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < kCommitTiles; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) prod[nt][mt][e] = Pa * sv[nt][mt][e];
+  }
+  __device__ __forceinline__ void store(int c0, const f32x4 (&prod)[kCommitTiles][kCommitTiles]) const {
     const bool lowh = l16 < 8;
 #pragma unroll
     for (int nt = 0; nt < kCommitTiles; ++nt)
@@ -179,9 +189,9 @@ struct CommitWave {
         f32x4 oX, oY, oYr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          oX[e] = Pa * sv[nt][2 * m][e] + prod[nt][2 * m][e];
+          oX[e] = prod[nt][2 * m][e];
           // a scalar copy: the bit cast of a vector element itself would read element 0
-          const float y = Pa * sv[nt][2 * m + 1][e] + prod[nt][2 * m + 1][e];
+          const float y = prod[nt][2 * m + 1][e];
           oY[e] = y;
           oYr[e] = __builtin_bit_cast(
               float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), kDppRowRor8, 0xf, 0xf,
@@ -273,14 +283,8 @@ __global__ __launch_bounds__(64) void commit_kernel(
   }
   __syncthreads();  // a single wave: orders the LDS writes before the reads
 
-  // The path products accumulate from zero; P_a S is added at the end.
+  // The path products accumulate onto P_a S.
   f32x4 prod[kCommitTiles][kCommitTiles];
-  auto clear = [&]() {
-#pragma unroll
-    for (int nt = 0; nt < kCommitTiles; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < kCommitTiles; ++mt) prod[nt][mt] = zero_f32x4();
-  };
   const bool hasB = cB < d_k;  // uniform
   if (cw.La <= kPathChunk) {
     // one step: every fragment of both blocks is requested, then block B's
@@ -296,23 +300,23 @@ __global__ __launch_bounds__(64) void commit_kernel(
     __builtin_amdgcn_sched_barrier(0);
     bf16x4 bh[kCommitTiles], bl[kCommitTiles];
     cw.u_frags(st, uraw, bh, bl);
-    clear();
+    cw.init(svA, prod);
     cw.accumulate(st, cA, krA, bh, bl, prod);
-    cw.store(cA, svA, prod);
+    cw.store(cA, prod);
     if (hasB) {
-      clear();
+      cw.init(svB, prod);
       cw.accumulate(st, cB, krB, bh, bl, prod);
-      cw.store(cB, svB, prod);
+      cw.store(cB, prod);
     }
   } else {
-    clear();
+    cw.init(svA, prod);
     cw.product(cA, 0, prod);
-    cw.store(cA, svA, prod);
+    cw.store(cA, prod);
     if (hasB) {
       cw.load_slot(cB, cA, svB);
-      clear();
+      cw.init(svB, prod);
       cw.product(cB, 0, prod);
-      cw.store(cB, svB, prod);
+      cw.store(cB, prod);
     }
   }
 }

@@ -54,7 +54,10 @@ namespace bole {
 // the kernel derives the tree's topology and this head's gate sums itself from
 // the parents and log-gates, with the arithmetic of bole_tree_prep, and
 // publishes them for the commit; the order/depth/anc/logP inputs are unused.
-template <int DT, bool FUSED, bool ONE, bool PREP, int SOLVE = kSolveBlocked>
+// COMMIT (with PREP): the previous round's accepted path of this layer is
+// committed into the slot first (CommitIO), and the verify reads the updated
+// state from registers.
+template <int DT, bool FUSED, bool ONE, bool PREP, int SOLVE = kSolveBlocked, bool COMMIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ logP, const float* __restrict__ beta,
@@ -64,9 +67,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int32_t* __restrict__ depth, const int32_t* __restrict__ tree_off,
     const int32_t* __restrict__ tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
     int32_t d_v, void* __restrict__ O, float* __restrict__ U, int32_t vecf, PrepIO prep,
-    uint32_t* __restrict__ err) {
+    uint32_t* __restrict__ err, CommitIO cm) {
   using SC = StageCfg<DT>;
   static_assert(!(FUSED && SOLVE == kSolveInverse), "W and M come from bole_factor_inverse");
+  static_assert(!COMMIT || (FUSED && PREP && SOLVE == kSolveBlocked), "commit inside tree verify");
   // O's own products (Q S_pre for B0, C U) carry the split low halves only for
   // float32 tokens; with bf16 tokens O is stored in bf16, and each product is
   // taken at that precision (hi parts: relative error near 2^-8, inside the
@@ -83,6 +87,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   __shared__ __align__(16) int rowNode[kMaxTree];
   __shared__ bf16x4 invs[4][2][64];  // (I + G_tt)^-1, A layout, hi / lo
   __shared__ int tree_ok;
+  // COMMIT: the first path step's key rows, transposed (key, position)
+  __shared__ __align__(16) typename PathCommit<DT>::KRaw ktile[COMMIT ? 16 * SC::KC : 1];
 
   const int NV = (d_v + kBV - 1) / kBV;
   const int lid = xcd_remap(blockIdx.x, B * H * NV);
@@ -93,17 +99,92 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const int g4 = lane >> 4, l16 = lane & 15;
 
   // independent per-tree scalars, fetched together
-  const int off = tree_off[b], end = tree_off[b + 1];
+  const int off_in = tree_off[b], end_in = tree_off[b + 1];
   const int td = PREP ? 0 : tree_depth[b];
   const int s = slot[b];
-  const int T = end - off;
-  if (off < 0 || end > N || T < 1 || T > kMaxTree) {
-    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_TREE_SIZE);
-    return;
+  const bool range_bad =
+      off_in < 0 || end_in > N || end_in - off_in < 1 || end_in - off_in > kMaxTree;
+  // COMMIT: a workgroup whose tree range is bad still commits.  It runs on as a
+  // stand-in one-node tree at node 0 (every access in bounds) that writes
+  // nothing and leaves at the rejected-tree exit.
+  const int off = COMMIT && range_bad ? 0 : off_in;
+  const int T = COMMIT && range_bad ? 1 : end_in - off_in;
+  // the previous round's accepted node and tree (COMMIT)
+  const int pa = COMMIT ? cm.accept[b] : -1;
+  const int po = COMMIT ? cm.tree_off[b] : 0;
+  const int pT = COMMIT ? cm.tree_off[b + 1] - po : 1;
+  const bool reporter = threadIdx.x == 0 && h == 0 && r == 0;
+  const bool slot_ok = s >= 0 && s < n_slots;
+  bool pend = false;  // uniform: a path to commit into the slot
+  if (COMMIT && pa != -1 && slot_ok) {
+    if (po < 0 || pT < 1 || pT > kMaxTree || po > cm.N - pT) {
+      if (reporter) report(err, BOLE_ERR_TREE_SIZE);
+    } else if (pa < 0 || pa >= pT) {
+      if (reporter) report(err, BOLE_ERR_BAD_ACCEPT);
+    } else {
+      pend = true;
+    }
+  }
+
+  // The state rows this lane holds: value column vcol of the slot, keys
+  // 32 kk + 8 g4 .. + 7 (the B fragments of phase A).
+  const int vloc = 16 * w + l16;
+  const int vcol = kBV * r + vloc;
+  const bool vin = vcol < d_v;
+  const int64_t srow = (((int64_t)(COMMIT && !slot_ok ? 0 : s) * H + h) * d_v + (vin ? vcol : 0)) * d_k;
+  const float* Srow = state_pool + srow;
+  // COMMIT: the wave's first slot row (uniform), where the committed rows go
+  float* const cbase =
+      cm.pool + (((int64_t)(slot_ok ? s : 0) * H + h) * d_v + kBV * r + 16 * w) * d_k;
+  float sx[SC::KC / 32][8];
+  // K positions past d_k read the row's first entries instead: they meet staged
+  // Q/K columns that are zero.  Lanes past d_v compute columns never stored.
+  auto load_s = [&](int kc0, int k0, int k1) {
+#pragma unroll
+    for (int kk = k0; kk < k1; ++kk) {
+      const int kidx = kc0 + 32 * kk + 8 * g4;
+      load_f32x8(Srow + (kidx < d_k ? kidx : 0), sx[kk]);
+    }
+  };
+
+  // COMMIT: the path (the accepted node's ancestor-or-self set) and the gate
+  // sums of the previous tree, one node per lane; loads clamped to node 0 when
+  // nothing is to be committed
+  PathCommit<DT> pc;
+  if (COMMIT) {
+    const int a0 = pend ? pa : 0, o0 = pend ? po : 0, t0 = pend ? pT : 1;
+    // the set is cut to the tree's nodes and never empty (an empty one, which
+    // only bad data can give, becomes the node itself), so every path position
+    // below La names a node of the previous tree
+    const uint64_t pm = cm.anc[o0 + a0] & (t0 == 64 ? ~0ull : ((1ull << t0) - 1ull));
+    pc.path = pm ? pm : 1ull << a0;
+    pc.lp = cm.logP[(int64_t)(o0 + min(lane, t0 - 1)) * H + h];
+    pc.kp = reinterpret_cast<const typename PathCommit<DT>::KRaw*>(cm.k) + (int64_t)o0 * H * d_k +
+            (int64_t)h * d_k;
+    pc.up = cm.U + (int64_t)o0 * H * d_v + (int64_t)h * d_v;
+    pc.ucol = vin ? vcol : 0;
+    pc.kstr = (int64_t)H * d_k;
+    pc.ustr = (int64_t)H * d_v;
+    pc.La = __popcll(pc.path);
+  }
+  // the whole commit of the lane's rows, for a workgroup that verifies nothing
+  constexpr int kNK = SC::KC / 32;
+  auto commit_only = [&]() {
+    load_s(0, 0, kNK);
+    pc.lpa = __shfl(pc.lp, pa);
+    pc.Pa = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, expf(pc.lpa))));
+    pc.steps(sx, ktile, 0, vin, g4, l16, d_k);
+    pc.store(cbase, sx, 0, kNK, vin, l16, g4, d_k);
+  };
+
+  if (range_bad) {
+    if (reporter) report(err, BOLE_ERR_TREE_SIZE);
+    if (!(COMMIT && pend)) return;
   }
   if (td < 0) return;  // rejected by tree preparation
-  if (s < 0 || s >= n_slots) {
-    if (threadIdx.x == 0 && h == 0 && r == 0) report(err, BOLE_ERR_BAD_SLOT);
+  if (!slot_ok) {
+    if (reporter) report(err, BOLE_ERR_BAD_SLOT);
     return;
   }
   const int nmt = (T + 15) >> 4;
@@ -146,10 +227,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 
   const int node_l = lane < T ? clamp_node(ord, T) : 0;
   u16x8 qkbuf[QkCfg<DT>::PER];
+  typename PathCommit<DT>::KPiece kpiece;
   if (PREP) {
     // the Q/K rows go out now, in node order, behind wave 0's small loads;
     // the topology is derived while they stream in
     qk_issue<DT, true>(qkbuf, q, k, nullptr, T, off, H, h, d_k, 0);
+    // COMMIT: the path's key rows, right behind them
+    if (COMMIT) kpiece = pc.tile_load(threadIdx.x, 0, d_k);
     __builtin_amdgcn_sched_barrier(0);
     if (w == 0) {
       // tree preparation for this (tree, head): topology (tree_topo.h), then
@@ -157,7 +241,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       // the float32 adds of bole_tree_prep's root-first running sum, in order
       const TreeTopo tp = tree_topology(lane, T, p_raw);
       const bool row_in = lane < T;
-      if (!tp.fail) {
+      if (!tp.fail && !(COMMIT && range_bad)) {
         // the ancestor-or-self set in level positions follows the same
         // recursion, apos_i = apos_parent(i) | bit(pos_i), in the same rounds
         const int pos = tp.pos;
@@ -192,8 +276,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         }
       }
       if (lane == 0) {
-        tree_ok = !tp.fail;
-        if (h == 0 && r == 0) {
+        tree_ok = !tp.fail && !(COMMIT && range_bad);
+        if (h == 0 && r == 0 && !(COMMIT && range_bad)) {
           prep.tree_depth[b] = tp.fail ? -1 : tp.dmax;
           if (tp.fail) report(err, tp.fail);
         }
@@ -204,28 +288,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     if (lane < T) posOf[node_l] = lane;
   }
   __syncthreads();  // rowNode visible (and with PREP every row table)
-  if (PREP && !tree_ok) return;  // uniform: a rejected tree
+  if (PREP && !tree_ok) {  // uniform: a rejected tree
+    if (COMMIT && pend) commit_only();
+    return;
+  }
+  if (COMMIT) {
+    // the lane's first 16 path positions and their U loads (the keys are
+    // staged in LDS with the Q/K rows)
+    pc.lpa = __shfl(pc.lp, pend ? pa : 0);
+    pc.Pa = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, expf(pc.lpa))));
+    pc.nodes(0, g4);
+    pc.issue_u();
+  }
 
   // everything below depends on the rows only.  Issue order: the Q/K rows
   // (needed first), the row scalars (wave 0), then the state slice and V,
   // which are consumed last.
   if (!PREP) qk_issue<DT>(qkbuf, q, k, rowNode, T, off, H, h, d_k, 0);
 
-  // S_pre rows of this wave's 16 value columns: first chunk's B fragments
-  const int vloc = 16 * w + l16;
-  const int vcol = kBV * r + vloc;
-  const bool vin = vcol < d_v;
-  const float* Srow = state_pool + (((int64_t)s * H + h) * d_v + (vin ? vcol : 0)) * d_k;
-  float sx[SC::KC / 32][8];
-  // K positions past d_k read the row's first entries instead: they meet staged
-  // Q/K columns that are zero.  Lanes past d_v compute columns never stored.
-  auto load_s = [&](int kc0, int k0, int k1) {
-#pragma unroll
-    for (int kk = k0; kk < k1; ++kk) {
-      const int kidx = kc0 + 32 * kk + 8 * g4;
-      load_f32x8(Srow + (kidx < d_k ? kidx : 0), sx[kk]);
-    }
-  };
   // nothing that waits on a load may be scheduled above this point: the Q/K
   // rows are in flight before the first wait
   __builtin_amdgcn_sched_barrier(0);
@@ -276,6 +357,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     qk_commit<DT, true>(stage, qkbuf, posOf, T);  // waits for the Q/K rows
   else
     qk_commit<DT>(stage, qkbuf);
+  if (COMMIT) pc.tile_store(ktile, threadIdx.x, kpiece);
   __syncthreads();  // staged rows and row tables visible
   // The state slice and V are requested only once the workgroup's Q/K rows are
   // in: the memory system serves concurrent requests interleaved, so issued
@@ -369,6 +451,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       }
     }
   }
+
+  // COMMIT: the first step's B fragments, formed once its U loads are in (they
+  // went out before the state slice), so that only the split fragments are
+  // held from here on
+  bf16x4 cbh, cbl;
+  if (COMMIT) pc.bfrag(vin, g4, cbh, cbl);
 
   // ---------------- Diagonal blocks: (I + G_tt)^-1 per 16-row tile --------
   // In level order G is strictly lower triangular, so each 16x16 diagonal
@@ -473,6 +561,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
 #pragma unroll
     for (int kk = 0; kk < SC::KC / 32; ++kk) {
+      if (COMMIT && pend && kk == 0) {  // uniform
+        // the committed state replaces S_pre in the lane's registers and goes
+        // back into the slot: the first half of the row chunks now, the second
+        // when phase A reaches it (so phase A on the first half overlaps the
+        // second half's arrival).  A path longer than 16 nodes takes every
+        // step on all chunks here.
+        pc.apply(sx, 0, kSHalf, true, cbh, cbl, l16, g4, d_k, ktile);
+        if (pc.La > 16) {
+          pc.apply(sx, kSHalf, kSChunks, true, cbh, cbl, l16, g4, d_k, ktile);
+          // the gate sums again (not held through the main path)
+          pc.lp = cm.logP[(int64_t)(po + min(lane, pT - 1)) * H + h];
+          pc.lpa = __shfl(pc.lp, pa);
+          pc.steps(sx, ktile, 16, vin, g4, l16, d_k);
+          pc.store(cbase, sx, 0, kSChunks, vin, l16, g4, d_k);
+        } else {
+          pc.store(cbase, sx, 0, kSHalf, vin, l16, g4, d_k);
+        }
+      }
+      if (COMMIT && pend && kk == kSHalf && pc.La <= 16) {  // uniform
+        pc.apply(sx, kSHalf, kSChunks, true, cbh, cbl, l16, g4, d_k, ktile);
+        pc.store(cbase, sx, kSHalf, kSChunks, vin, l16, g4, d_k);
+      }
       if (kc0 + 32 * kk < d_k) {
         bf16x8 b_hi, b_lo;
         split_bf16x8(sx[kk], b_hi, b_lo);
@@ -750,23 +860,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 }  // namespace bole
 
 namespace {
-template <int DT, bool FUSED, bool ONE, bool PREP = false, int SOLVE = bole::kSolveBlocked>
+template <int DT, bool FUSED, bool ONE, bool PREP = false, int SOLVE = bole::kSolveBlocked,
+          bool COMMIT = false>
 int launch_verify_t(const void* q, const void* k, const void* v, const float* logP,
                     const float* beta, const float* state_pool, int32_t n_slots,
                     const int32_t* slot, const float* G, const float* C, const uint64_t* anc,
                     const int32_t* order, const int32_t* depth, const int32_t* tree_off,
                     const int32_t* tree_depth, int32_t B, int32_t N, int32_t H, int32_t d_k,
                     int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s,
-                    bole::PrepIO prep = bole::PrepIO{}) {
+                    bole::PrepIO prep = bole::PrepIO{}, bole::CommitIO cm = bole::CommitIO{}) {
   const int NV = (d_v + bole::kBV - 1) / bole::kBV;
   const dim3 grid(B * H * NV), block(bole::kThreads);
   const int esize = DT == BOLE_BF16 ? 2 : 4;
   const bool v_ok = d_v % (16 / esize) == 0 && (uintptr_t)v % 16 == 0;
   const bool out_ok = d_v % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)O % (4 * esize) == 0;
   const int vecf = (v_ok ? bole::kVecV : 0) | (out_ok ? bole::kVecOut : 0);
-  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE>), grid, block, 0, s, q, k, v,
-                     logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err);
+  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT>), grid, block, 0, s, q,
+                     k, v, logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
+                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err, cm);
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 
@@ -869,4 +980,24 @@ extern "C" int bole_tree_verify_launch(int32_t dtype, const void* q, const void*
   return launch_verify_t<BOLE_F32, true, true, true>(
       q, k, v, nullptr, beta, state_pool, n_slots, slot, nullptr, nullptr, nullptr, nullptr,
       nullptr, tree_off, nullptr, B, N, H, d_k, d_v, O, U, err, s, prep);
+}
+
+extern "C" int bole_commit_tree_verify_launch(
+    int32_t dtype, const void* q, const void* k, const void* v, const int32_t* parent,
+    const float* log_gamma, const float* beta, float* state_pool, int32_t n_slots,
+    const int32_t* slot, const int32_t* tree_off, int32_t B, int32_t N, int32_t H, int32_t d_k,
+    int32_t d_v, void* O, float* U, int32_t* depth, uint64_t* anc, int32_t* order,
+    int32_t* tree_depth, float* logP, const void* prev_k, const float* prev_U,
+    const float* prev_logP, const uint64_t* prev_anc, const int32_t* prev_tree_off,
+    const int32_t* prev_accept, int32_t prev_N, uint32_t* err, hipStream_t s) {
+  const bole::PrepIO prep{parent, log_gamma, depth, anc, order, tree_depth, logP};
+  const bole::CommitIO cm{state_pool, prev_k,        prev_U,      prev_logP,
+                          prev_anc,   prev_tree_off, prev_accept, prev_N};
+  if (dtype == BOLE_BF16)
+    return launch_verify_t<BOLE_BF16, true, true, true, bole::kSolveBlocked, true>(
+        q, k, v, nullptr, beta, state_pool, n_slots, slot, nullptr, nullptr, nullptr, nullptr,
+        nullptr, tree_off, nullptr, B, N, H, d_k, d_v, O, U, err, s, prep, cm);
+  return launch_verify_t<BOLE_F32, true, true, true, bole::kSolveBlocked, true>(
+      q, k, v, nullptr, beta, state_pool, n_slots, slot, nullptr, nullptr, nullptr, nullptr,
+      nullptr, tree_off, nullptr, B, N, H, d_k, d_v, O, U, err, s, prep, cm);
 }

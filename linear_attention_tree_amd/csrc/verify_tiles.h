@@ -1,6 +1,8 @@
 // Tile geometry and fragment helpers shared by the verify kernels of libbole.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace bole {
@@ -58,6 +60,196 @@ struct PrepIO {
   int32_t* order;         // [N]
   int32_t* tree_depth;    // [B]
   float* logP;            // [N, H] of the layer
+};
+
+// The previous round's accepted path, committed into the slot by the verify
+// kernel before it reads the state (bole_commit_tree_verify).  Request b of the
+// round is request b of the previous round, with the same slot.
+struct CommitIO {
+  float* pool;              // [n_slots, H, d_v, d_k] state pool, updated in place
+  const void* k;            // [N0, H, d_k] the previous round's keys (token dtype)
+  const float* U;           // [N0, H, d_v] the previous round's U
+  const float* logP;        // [N0, H] the previous round's gate sums
+  const uint64_t* anc;      // [N0] ancestor-or-self sets of the previous forest
+  const int32_t* tree_off;  // [B + 1] the previous forest's offsets
+  const int32_t* accept;    // [B] accepted local node, -1 for nothing to commit
+  int32_t N;                // N0
+};
+
+// The n-th (from 0) set bit of m, by binary search over halves.  If m has n
+// or fewer set bits the result is some position in 0..63.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int half = 32; half >= 1; half >>= 1) {
+    const uint64_t low = m & ((1ull << half) - 1ull);
+    const int c = __popcll(low);
+    const bool up = n >= c;
+    n -= up ? c : 0;
+    m = up ? m >> half : low;
+    pos += up ? half : 0;
+  }
+  return pos;
+}
+
+// The accepted-path update S <- P_a S + sum_j (P_a / P_j) U_j k_j^T on the state
+// rows one verify lane holds: value column v, keys 32 kk + 8 g .. + 7 for each
+// 32-key chunk kk.  It takes the MFMA steps of bole_commit_path on the same
+// operands, so both produce the same bits.  Each 8-key group is two 16x16
+// accumulator tiles whose row m is key 32 kk + 8 (m / 4) + 4 half + m % 4, so a
+// lane's accumulator holds exactly its four keys of the group: the update needs
+// no data movement between lanes.  The A operand (keys) of a lane is row m =
+// l16 of that tile at its four path positions, the B operand (P_a/P_j) U_j[v]
+// at the same positions, split hi + lo.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// store_sc1 with a uniform base address (scalar registers) and a 32-bit byte
+// offset per lane: only the offset occupies a vector register.
+__device__ __forceinline__ void store_sc1_at(float* base, uint32_t off_bytes, const f32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, %2 sc1" : : "v"(off_bytes), "v"(v), "s"(base) : "memory");
+}
+
+template <int DT>
+struct PathCommit {
+  using KRaw = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
+  using KVec = std::conditional_t<DT == BOLE_BF16, u16x4, u32x4>;
+  static constexpr int NK = StageCfg<DT>::KC / 32;  // 32-key chunks per lane
+  const KRaw* kp;   // keys of head h at node 0 of the previous tree
+  const float* up;  // U of head h at node 0 (uniform; the lane adds its column)
+  int64_t kstr, ustr;
+  int ucol;         // the lane's value column (clamped into the row)
+  uint64_t path;
+  float lp, lpa, Pa;
+  int La;
+  int node[4];      // the lane's path positions of a step, as node ids
+  int kc_;          // the step's first position
+  float wt[4];      // P_a / P_j
+  float uraw[4];    // U_j[v]
+
+  static __device__ __forceinline__ int key(int kk, int half, int l16) {
+    return 32 * kk + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
+  }
+  // positions kc + 4 g + e of the step: node ids (position 0 past the path)
+  __device__ __forceinline__ void nodes(int kc, int g4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = kc + 4 * g4 + e;
+      node[e] = nth_set_bit(path, p < La ? p : 0);
+    }
+    kc_ = kc;
+  }
+  // bit e: the lane's position e of the step is on the path
+  __device__ __forceinline__ uint32_t lmask(int g4) const {
+    const int left = La - kc_ - 4 * g4;
+    return left >= 4 ? 15u : (left > 0 ? (1u << left) - 1u : 0u);
+  }
+  // their weights, and the U loads (unconditional)
+  __device__ __forceinline__ void issue_u() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wt[e] = expf(lpa - __shfl(lp, node[e]));
+      uraw[e] = up[(int64_t)node[e] * ustr + ucol];
+    }
+  }
+  // the step's B fragments: (P_a/P_j) U_j[v], split hi + lo
+  __device__ __forceinline__ void bfrag(bool vin, int g4, bf16x4& bh, bf16x4& bl) const {
+    const uint32_t lm = lmask(g4);
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, wt[e] * uraw[e]) &
+                                           keep(vin && ((lm >> e) & 1u)));
+    split_bf16x4(x, bh, bl);
+  }
+  // A step's key rows are staged once per workgroup, transposed: kt[c][p] is
+  // key c of path position p (16 positions), so a lane's A fragment (four
+  // consecutive positions of one key) is one LDS read.  Thread t loads 8 bytes
+  // of position kc + t / 32 (unconditionally, a key past d_k reads key 0) and
+  // writes them once they land.
+  static constexpr int KPT = 8 / sizeof(KRaw);  // keys per thread
+  using KPiece = std::conditional_t<DT == BOLE_BF16, u16x4, uint2>;
+  __device__ __forceinline__ KPiece tile_load(int t, int kc, int d_k) const {
+    const int p = kc + (t >> 5), c = KPT * (t & 31);
+    const int n = nth_set_bit(path, p < La ? p : 0);
+    return *reinterpret_cast<const KPiece*>(kp + (int64_t)n * kstr + (c < d_k ? c : 0));
+  }
+  __device__ __forceinline__ void tile_store(KRaw* kt, int t, const KPiece& v) const {
+    const int p = t >> 5, c = KPT * (t & 31);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kt[(c + i) * 16 + p] = v[i];
+  }
+  // the whole tile for step kc, by every thread of the workgroup (uniform)
+  __device__ __forceinline__ void stage(KRaw* kt, int kc, int d_k) const {
+    const KPiece v = tile_load(threadIdx.x, kc, d_k);
+    __syncthreads();  // the previous step's tile is no longer read
+    tile_store(kt, threadIdx.x, v);
+    __syncthreads();
+  }
+
+  // one step of 16 path positions onto chunks [k0, k1) of the lane's rows; the
+  // first starts the accumulation from P_a S.  Keys from the staged tile.
+  __device__ __forceinline__ void apply(float (&sx)[NK][8], int k0, int k1, bool first,
+                                        const bf16x4& bh, const bf16x4& bl, int l16, int g4, int d_k,
+                                        const KRaw* kt) const {
+    const uint32_t lm = lmask(g4);
+#pragma unroll
+    for (int kk = k0; kk < k1; ++kk)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int c = key(kk, half, l16);
+        const uint32_t kok = keep(c < d_k);
+        const KVec kv = *reinterpret_cast<const KVec*>(kt + c * 16 + 4 * g4);
+        bf16x4 ah, al;
+        if (DT == BOLE_BF16) {
+          u16x4 raw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) raw[e] = kv[e] & (uint16_t)(keep((lm >> e) & 1u) & kok);
+          ah = __builtin_bit_cast(bf16x4, raw);
+        } else {
+          f32x4 kx;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            kx[e] = __builtin_bit_cast(float, kv[e] & (keep((lm >> e) & 1u) & kok));
+          split_bf16x4(kx, ah, al);
+        }
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = first ? Pa * sx[kk][4 * half + i] : sx[kk][4 * half + i];
+        acc = mfma16_bf16(ah, bh, acc);
+        acc = mfma16_bf16(ah, bl, acc);
+        if (DT == BOLE_F32) acc = mfma16_bf16(al, bh, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sx[kk][4 * half + i] = acc[i];
+      }
+  }
+  // the steps from position kc0 on, on every chunk, each with its own staged
+  // tile (uniform over the workgroup: it has barriers)
+  __device__ __forceinline__ void steps(float (&sx)[NK][8], KRaw* kt, int kc0, bool vin, int g4,
+                                        int l16, int d_k) {
+    for (int kc = kc0; kc < La; kc += 16) {
+      stage(kt, kc, d_k);
+      nodes(kc, g4);
+      issue_u();
+      bf16x4 bh, bl;
+      bfrag(vin, g4, bh, bl);
+      apply(sx, 0, NK, kc == 0, bh, bl, l16, g4, d_k, kt);
+    }
+  }
+  // committed chunks [k0, k1) back into the slot (written through to HBM, as
+  // the commit's stores are): base is the wave's first row (uniform), the lane
+  // adds its own row
+  __device__ __forceinline__ void store(float* base, const float (&sx)[NK][8], int k0, int k1, bool vin,
+                                        int l16, int g4, int d_k) const {
+#pragma unroll
+    for (int kk = k0; kk < k1; ++kk) {
+      const int c = 32 * kk + 8 * g4;
+      if (vin && c < d_k) {
+        const uint32_t o = 4u * (uint32_t)(l16 * d_k + c);
+        store_sc1_at(base, o, f32x4{sx[kk][0], sx[kk][1], sx[kk][2], sx[kk][3]});
+        store_sc1_at(base, o + 16u, f32x4{sx[kk][4], sx[kk][5], sx[kk][6], sx[kk][7]});
+      }
+    }
+  }
 };
 
 // How the verify kernel solves (I + G) U = R.  All three are exact (the closed

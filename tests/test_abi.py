@@ -34,6 +34,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_symbols()
     assert set(names) == {"bole_tree_prep", "bole_gc_workspace_bytes", "bole_factor_gc",
                           "bole_verify", "bole_factor_verify", "bole_tree_verify",
+                          "bole_commit_tree_verify",
                           "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
                           "bole_commit_path", "bole_tree_conv", "bole_conv_commit",
                           "bole_forest_build", "bole_forest_workspace_bytes",
@@ -47,7 +48,8 @@ def test_internal_launchers_are_hidden(L):
     for n in ("bole_verify_launch", "bole_factor_gc_launch", "bole_commit_launch",
               "bole_verify_neumann_launch", "bole_verify_inverse_launch",
               "bole_factor_inverse_launch", "bole_forest_build_launch",
-              "bole_tree_verify_launch", "bole_tree_conv_launch", "bole_conv_commit_launch"):
+              "bole_tree_verify_launch", "bole_commit_tree_verify_launch",
+              "bole_tree_conv_launch", "bole_conv_commit_launch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
 
@@ -127,6 +129,26 @@ def test_tree_verify_argument_errors(L):
     assert call(dk=256) == E_UNSUPPORTED
     assert call(dtype=0, dk=128) == E_UNSUPPORTED
     assert call(dv=40) == E_UNSUPPORTED
+
+
+def test_commit_tree_verify_argument_errors(L):
+    f = L.bole_commit_tree_verify
+    A = ctypes.c_void_p(0x1000)          # 8-byte aligned, never dereferenced
+    U = ctypes.c_void_p(0x1004)          # not 8-byte aligned
+
+    def call(dtype=1, dk=128, dv=128, pool=A, prev_k=A, accept=A, B=1, H=1, N0=1):
+        return f(dtype, A, A, A, A, A, A, pool, 1, A, A, B, 1, H, dk, dv,
+                 A, A, A, A, A, A, A, prev_k, A, A, A, A, accept, N0, None, None)
+
+    assert call(dtype=3) == E_DTYPE
+    assert call(pool=None) == E_NULL
+    assert call(prev_k=None) == E_NULL
+    assert call(accept=None) == E_NULL
+    assert call(B=0) == E_SHAPE
+    assert call(N0=0) == E_SHAPE
+    assert call(dk=256) == E_UNSUPPORTED
+    assert call(dtype=0, dk=128) == E_UNSUPPORTED
+    assert call(prev_k=U) == E_UNSUPPORTED
 
 
 def test_tree_conv_argument_errors(L):
