@@ -30,13 +30,15 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-PROFILE_COUNTERS = os.path.join(PROFILES, "bole_tree_verify_target_counters.json")
+PROFILE_COUNTERS = os.path.join(PROFILES, "bole_commit_tree_verify_target_counters.json")
 KERNEL_SOURCE_NAMES = ("verify.hip", "verify_tiles.h", "tree_topo.h", "common.h")
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_tree_amd", "csrc", f)
                   for f in KERNEL_SOURCE_NAMES]
-# the bf16 verify kernel with preparation inside, which the default step
-# launches (name as rocprofv3 prints it)
-DOMINANT_KERNEL = "verify_kernel<1, true, true, true, 0>"
+# the bf16 verify kernel with preparation and the previous round's commit
+# inside, which the default step launches (name as rocprofv3 prints it)
+DOMINANT_KERNEL = "verify_kernel<1, true, true, true, 0, true>"
+# the same without the commit (bole_tree_verify)
+TREE_VERIFY_KERNEL = "verify_kernel<1, true, true, true, 0, false>"
 
 
 def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
@@ -55,7 +57,32 @@ def tree_verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
         sum(T * (4 * H + 4 + 16) + 4 for T in sizes))
 
 
+def path_lengths(forest):
+    """Nodes on each request's accepted path (root to accepted node), for the
+    requests that accept one."""
+    out = []
+    for b, a in enumerate(forest.accept):
+        if a < 0:
+            continue
+        o, n, j = forest.tree_off[b], 1, int(a)
+        while forest.parent[o + j] >= 0:
+            j, n = int(forest.parent[o + j]), n + 1
+        out.append(n)
+    return out
+
+
+def commit_tree_verify_algorithmic_bytes(sizes, prev_forest, H, d_k, d_v, e):
+    """bole_commit_tree_verify: bole_tree_verify's bytes plus the commit's own:
+    each committed slot written once (it is read once, already counted), the
+    accepted path's key, U and logP entries, the accepted node's ancestor set,
+    and the previous offsets and accepted nodes."""
+    extra = sum(H * (4 * d_k * d_v + la * (e * d_k + 4 * d_v + 4)) + 8
+                for la in path_lengths(prev_forest))
+    return tree_verify_algorithmic_bytes(sizes, H, d_k, d_v, e) + int(extra) + 12 * len(sizes)
+
+
 DOMINANT = {  # path -> (launch name, algorithmic bytes of one launch)
+    "deferred": ("commit_tree_verify", None),  # bytes depend on the previous round
     "tree": ("tree_verify", tree_verify_algorithmic_bytes),
     "fused": ("factor_verify", verify_algorithmic_bytes),
     "split": ("verify", verify_algorithmic_bytes),
@@ -108,7 +135,10 @@ def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
     cfg = W.CONFIGS["target"]
     forests = [W.make_forest(cfg, seed) for seed in range(4)]
     algo = {
-        "bole::verify_kernel<1, true, true, true, 0>": np.mean(
+        "bole::" + DOMINANT_KERNEL: np.mean(
+            [commit_tree_verify_algorithmic_bytes(f.sizes(), forests[i - 1], cfg.H, cfg.d_k,
+                                                  cfg.d_v, 2) for i, f in enumerate(forests)]),
+        "bole::" + TREE_VERIFY_KERNEL: np.mean(
             [tree_verify_algorithmic_bytes(f.sizes(), cfg.H, cfg.d_k, cfg.d_v, 2) for f in forests]),
         "bole::commit_kernel<1>": np.mean(
             [commit_algorithmic_bytes(f, 1, cfg.H, cfg.d_k, cfg.d_v, 2) for f in forests]),
@@ -196,8 +226,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     f_fetch, f_write = calib_kib / copy_fetch, calib_kib / copy_write
     traffic = (fetch * f_fetch + write * f_write) * 1024.0
     cfg = W.CONFIGS["target"]
-    algo = np.mean([tree_verify_algorithmic_bytes(W.make_forest(cfg, seed).sizes(), cfg.H,
-                                                  cfg.d_k, cfg.d_v, 2) for seed in range(4)])
+    forests = [W.make_forest(cfg, seed) for seed in range(4)]
+    algo = np.mean([commit_tree_verify_algorithmic_bytes(f.sizes(), forests[i - 1], cfg.H, cfg.d_k,
+                                                         cfg.d_v, 2) for i, f in enumerate(forests)])
     rec = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": kernel_source_hash(),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [n_f, n_w], "copy_mib": calib_mib,
@@ -207,7 +238,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     with open(PROFILE_COUNTERS, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
-    md = ["# HBM traffic of `bole_tree_verify`, target workload (rocprofv3 --pmc)", "",
+    md = ["# HBM traffic of `bole_commit_tree_verify`, target workload (rocprofv3 --pmc)", "",
           "Commands (one counter per pass; each pass first copies "
           f"{calib_mib} MiB device-to-device for the calibration):", "", "```",
           commands["fetch"], commands["write"], "```", "",
@@ -223,7 +254,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
           f"Kernel source hash: `{rec['kernel_source_hash']}` ({', '.join(KERNEL_SOURCE_NAMES)}); "
           "bench.py reports `traffic` only while it matches.", ""]
     md += all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write)
-    with open(os.path.join(PROFILES, "bole_tree_verify_target_counters.md"), "w") as fh:
+    with open(os.path.join(PROFILES, "bole_commit_tree_verify_target_counters.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(rec))
 
@@ -316,12 +347,23 @@ def launch(s, bole, which):
     elif which == "commit":
         bole.bole_commit_path(s.pool, s.slot, s.k, s.U, lp, t.anc, t.tree_off, s.accept,
                               s.rnd.err)
+    elif which == "commit_tree_verify":
+        # the previous input set's round is committed into this set's slots:
+        # the same work as a serving loop's previous round of the same requests
+        p, pt = s.prev, s.prev.rnd.topo
+        bole.bole_commit_tree_verify(s.q, s.k, s.v, t.parent, s.g[0], s.beta, s.pool, s.slot,
+                                     t.tree_off, s.O, s.U, t.depth, t.anc, t.order, t.tree_depth,
+                                     lp, p.k, p.U, p.logP[0], pt.anc, pt.tree_off, p.accept,
+                                     s.rnd.err)
     else:
         raise ValueError(which)
 
 
 STEPS = {
-    # preparation, G/C and verify in one launch, then the commit (the default)
+    # the previous round's commit, preparation, G/C and verify in one launch
+    # (the default): one round's commit and one round's verify per step
+    "deferred": ("commit_tree_verify",),
+    # preparation, G/C and verify in one launch, then the commit
     "tree": ("tree_verify", "commit"),
     # preparation on its own, G/C produced and consumed in one launch
     "fused": ("tree_prep", "factor_verify", "commit"),
@@ -714,12 +756,14 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="target", choices=sorted(W.CONFIGS))
     ap.add_argument("--sets", type=int, default=4, help="rotated independent input sets")
-    ap.add_argument("--path", default="tree", choices=sorted(STEPS),
-                    help="tree: tree_verify + commit; fused: prep + factor_verify + commit; "
+    ap.add_argument("--path", default="deferred", choices=sorted(STEPS),
+                    help="deferred: commit_tree_verify (the previous round's commit inside this "
+                         "round's verify); tree: tree_verify + commit; "
+                         "fused: prep + factor_verify + commit; "
                          "split: the four calls; split_neumann, split_inverse: the four calls "
                          "with the other exact solves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -763,7 +807,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.sets < 2:
+        raise SystemExit("--sets must be at least 2 (a step commits the previous set's round)")
     sets = [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(args.sets)]
+    for i, s_ in enumerate(sets):
+        s_.prev = sets[i - 1]  # the round before this one, in the rotation
     e = 2 if cfg.dtype == "bf16" else 4
 
     for i in range(args.warmup):
@@ -786,8 +834,12 @@ def main():
         return capture(torch, lambda: [run_step(sets[i % len(sets)], bole, p) for i in range(R)])
 
     def time_k_steps(p, k, singles_p):
-        """Exactly k steps: k // R rotation replays, then the rest one by one."""
+        """Exactly k steps: k // R rotation replays, then the rest one by one,
+        after an untimed pre-roll of the same graph (the GPU otherwise enters
+        the timed region idle, right after the host-side captures)."""
         rot = rotation(p)
+        for _ in range(max(1, min(k, 200) // R)):
+            rot.replay()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -810,7 +862,7 @@ def main():
     # per-kernel averages: each kernel alone, 4 x len(sets) launches per graph
     # over the rotated sets (same inputs, same stream)
     kernels = ("tree_prep", "factor_gc", "verify", "factor_verify", "tree_verify", "commit",
-               "verify_neumann", "factor_inverse", "verify_inverse")
+               "commit_tree_verify", "verify_neumann", "factor_inverse", "verify_inverse")
     avg = {}
     for which in kernels:
         n_in = 4 * len(sets)
@@ -830,12 +882,16 @@ def main():
 
     nodes = sum(s.forest.N for s in sets) / len(sets)
     value = nodes * cfg.H / (ms_step * 1e-3)
-    vbytes = np.mean([bytes_fn(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
+    if args.path == "deferred":
+        vbytes = np.mean([commit_tree_verify_algorithmic_bytes(s.sizes, s.prev.forest, cfg.H,
+                                                               cfg.d_k, cfg.d_v, e) for s in sets])
+    else:
+        vbytes = np.mean([bytes_fn(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
     achieved = vbytes / (avg[dominant] * 1e-3) / 1e9
     # a plain copy over the same footprint as the rotated input sets
     copy_gbs = copy_bandwidth(torch, dev, int(vbytes * len(sets)), 20)
     # the committed counter record is the default path's dominant kernel
-    traffic = traffic_from_profile(kernel_source_hash()) if args.path == "tree" else None
+    traffic = traffic_from_profile(kernel_source_hash()) if args.path == "deferred" else None
 
     out = {
         "metric": "tree nodes x heads verified/sec per GDN layer",
@@ -853,7 +909,10 @@ def main():
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} trees x T={cfg.T} nodes (random recursive, "
                         f"depth<={cfg.D}), H={cfg.H}, d_k=d_v={cfg.d_k}, {cfg.dtype} q/k/v, "
-                        f"f32 gates and state; step = {' + '.join(STEPS[args.path])}",
+                        f"f32 gates and state; step = {' + '.join(STEPS[args.path])}"
+                        + (" (this round's verify with the previous round's accepted-path "
+                           "commit inside: one commit and one verify per step)"
+                           if args.path == "deferred" else ""),
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
             "nodes": nodes, "input_sets": len(sets), "path": args.path,
             "timing": "HIP graph replays: 16 captured steps per graph; kernels: 16 launches per graph",

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // COMMIT: the wave's first slot row (uniform), where the committed rows go
   float* const cbase =
       cm.pool + (((int64_t)(slot_ok ? s : 0) * H + h) * d_v + kBV * r + 16 * w) * d_k;
+  const int cvl = d_v - (kBV * r + 16 * w);  // rows of the wave inside d_v
   float sx[SC::KC / 32][8];
   // K positions past d_k read the row's first entries instead: they meet staged
   // Q/K columns that are zero.  Lanes past d_v compute columns never stored.
@@ -157,7 +158,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     // only bad data can give, becomes the node itself), so every path position
     // below La names a node of the previous tree
     const uint64_t pm = cm.anc[o0 + a0] & (t0 == 64 ? ~0ull : ((1ull << t0) - 1ull));
-    pc.path = pm ? pm : 1ull << a0;
+    const uint64_t pth = pm ? pm : 1ull << a0;
+    // uniform (one load address for the whole workgroup), held in scalar
+    // registers so that branches on the path length are scalar branches
+    pc.path = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(pth >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pth);
     pc.lp = cm.logP[(int64_t)(o0 + min(lane, t0 - 1)) * H + h];
     pc.kp = reinterpret_cast<const typename PathCommit<DT>::KRaw*>(cm.k) + (int64_t)o0 * H * d_k +
             (int64_t)h * d_k;
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     pc.Pa = __builtin_bit_cast(
         float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, expf(pc.lpa))));
     pc.steps(sx, ktile, 0, vin, g4, l16, d_k);
-    pc.store(cbase, sx, 0, kNK, vin, l16, g4, d_k);
+    pc.store(cbase, sx, 0, kNK, cvl, l16, g4, d_k);
   };
 
   if (range_bad) {
@@ -574,14 +579,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
           pc.lp = cm.logP[(int64_t)(po + min(lane, pT - 1)) * H + h];
           pc.lpa = __shfl(pc.lp, pa);
           pc.steps(sx, ktile, 16, vin, g4, l16, d_k);
-          pc.store(cbase, sx, 0, kSChunks, vin, l16, g4, d_k);
+          pc.store(cbase, sx, 0, kSChunks, cvl, l16, g4, d_k);
         } else {
-          pc.store(cbase, sx, 0, kSHalf, vin, l16, g4, d_k);
+          pc.store(cbase, sx, 0, kSHalf, cvl, l16, g4, d_k);
         }
       }
       if (COMMIT && pend && kk == kSHalf && pc.La <= 16) {  // uniform
         pc.apply(sx, kSHalf, kSChunks, true, cbh, cbl, l16, g4, d_k, ktile);
-        pc.store(cbase, sx, kSHalf, kSChunks, vin, l16, g4, d_k);
+        pc.store(cbase, sx, kSHalf, kSChunks, cvl, l16, g4, d_k);
       }
       if (kc0 + 32 * kk < d_k) {
         bf16x8 b_hi, b_lo;

@@ -103,10 +103,17 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
 // at the same positions, split hi + lo.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// store_sc1 with a uniform base address (scalar registers) and a 32-bit byte
-// offset per lane: only the offset occupies a vector register.
-__device__ __forceinline__ void store_sc1_at(float* base, uint32_t off_bytes, const f32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, %2 sc1" : : "v"(off_bytes), "v"(v), "s"(base) : "memory");
+// A 16-byte store at a uniform base address plus a 32-bit byte offset per lane
+// (the compiler keeps the base in scalar registers).
+__device__ __forceinline__ void store_at(float* base, uint32_t off_bytes, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off_bytes) = v;
+}
+
+// 16 wait states, kept in place by scheduling barriers.
+__device__ __forceinline__ void swap_gap() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int DT>
@@ -235,18 +242,61 @@ struct PathCommit {
       apply(sx, 0, NK, kc == 0, bh, bl, l16, g4, d_k, kt);
     }
   }
-  // committed chunks [k0, k1) back into the slot (written through to HBM, as
-  // the commit's stores are): base is the wave's first row (uniform), the lane
-  // adds its own row
-  __device__ __forceinline__ void store(float* base, const float (&sx)[NK][8], int k0, int k1, bool vin,
-                                        int l16, int g4, int d_k) const {
+  // Committed chunks [k0, k1) back into the slot, as whole 128-byte lines (the
+  // state rows leave in the middle of the kernel, so ordinary write-back stores
+  // measured faster than writing through: 24.5 against 26.0 us at the target
+  // shape; 16-byte pieces at a 32-byte stride, written through, took 31.9).  A
+  // chunk of row v
+  // is one line, held as 32 bytes by each of the four lanes g = 0..3 of column
+  // v.  Two row swaps between the lane's halves (16-lane rows, then 32-lane
+  // halves) leave each lane with the line's 16-byte pieces g (first half) and
+  // 4 + g (second half); a rotation by 8 within each 16-lane row then lets one
+  // store cover rows 0..7 of the wave's 16 and the next rows 8..15, each line
+  // whole.  base is the wave's first row (uniform).
+  __device__ __forceinline__ void store(float* base, const float (&sx)[NK][8], int k0, int k1,
+                                        int v_left, int l16, int g4, int d_k) const {
+    const bool low = l16 < 8;
+    const int row1 = l16 & 7, row2 = row1 + 8;
+    const int c_half = (low ? 0 : 16) + 4 * g4;  // the lane's key within a chunk
 #pragma unroll
     for (int kk = k0; kk < k1; ++kk) {
-      const int c = 32 * kk + 8 * g4;
-      if (vin && c < d_k) {
-        const uint32_t o = 4u * (uint32_t)(l16 * d_k + c);
-        store_sc1_at(base, o, f32x4{sx[kk][0], sx[kk][1], sx[kk][2], sx[kk][3]});
-        store_sc1_at(base, o + 16u, f32x4{sx[kk][4], sx[kk][5], sx[kk][6], sx[kk][7]});
+      // Explicit wait states before the lines are read out of the update's
+      // accumulators and between the swap stages (each swap writes both of its
+      // registers): with only the compiler's own spacing, the last four lanes
+      // of some rows stored stale values in some runs.
+      uint32_t x0[4], x1[4];
+      swap_gap();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, sx[kk][i]),
+                                                          __builtin_bit_cast(uint32_t, sx[kk][4 + i]),
+                                                          false, false);
+        x0[i] = s16[0];
+        x1[i] = s16[1];
+      }
+      swap_gap();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto s32 = __builtin_amdgcn_permlane32_swap(x0[i], x1[i], false, false);
+        x0[i] = s32[0];  // line piece g4 (keys 4 g4 .. + 3)
+        x1[i] = s32[1];  // line piece 4 + g4
+      }
+      swap_gap();
+      f32x4 d1, d2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // both halves rotate by 8 within the 16-lane row and the select comes
+        // after the move (a select on the rotated operand was folded away by
+        // the compiler, which is wrong for a cross-lane move)
+        const int r0 = __builtin_amdgcn_update_dpp(0, (int)x0[i], 0x128, 0xf, 0xf, false);
+        const int r1 = __builtin_amdgcn_update_dpp(0, (int)x1[i], 0x128, 0xf, 0xf, false);
+        d1[i] = __builtin_bit_cast(float, low ? (int)x0[i] : r1);
+        d2[i] = __builtin_bit_cast(float, low ? r0 : (int)x1[i]);
+      }
+      const int c = 32 * kk + c_half;
+      if (c - 4 * g4 < d_k) {  // the 16-key half is inside d_k (d_k is a multiple of 16)
+        if (row1 < v_left) store_at(base, 4u * (uint32_t)(row1 * d_k + c), d1);
+        if (row2 < v_left) store_at(base, 4u * (uint32_t)(row2 * d_k + c), d2);
       }
     }
   }

@@ -24,5 +24,5 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_paths_and_workloads():
     r = run("--help")
     assert r.returncode == 0
-    for word in ("tree", "fused", "split_neumann", "split_inverse", "multilayer"):
+    for word in ("deferred", "tree", "fused", "split_neumann", "split_inverse", "multilayer"):
         assert word in r.stdout, word
