@@ -637,9 +637,13 @@ def time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K):
 def round_main(cfg, args, torch, TreeRound, bole, dev):
     """One step = one verification round over cfg.L layers: the per-layer
     verify launches, then one commit over all layers (in place, so each round
-    verifies against the states the previous round committed)."""
+    verifies against the states the previous round committed).  With --path
+    deferred each layer's launch carries that layer's commit of the previous
+    round instead (bole_commit_tree_verify) and there is no separate commit;
+    the per-round outputs (U, logP, topology) alternate between two buffer
+    sets, so a round reads the previous one's while writing its own."""
     if args.path.startswith("split"):
-        raise SystemExit("the multi-layer round runs --path tree or --path fused")
+        raise SystemExit("the multi-layer round runs --path deferred, tree or fused")
     L, H = cfg.L, cfg.H
     f = W.make_forest(cfg, 0)
     B, N = f.B, f.N
@@ -671,32 +675,66 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
     def commit():
         bole.bole_commit_path(pool, slot, x.k, U, logP, t.anc, t.tree_off, accept, rnd.err)
 
+    # the second buffer set of the deferred rounds (the first is U, logP, t)
+    U2 = torch.empty_like(U)
+    logP2 = torch.empty_like(logP)
+    topo2 = [torch.empty_like(a) for a in (t.depth, t.anc, t.order, t.tree_depth)]
+    sets_d = [(U, logP, (t.depth, t.anc, t.order, t.tree_depth)), (U2, logP2, tuple(topo2))]
+
+    def deferred_round(cur):
+        (Uc, lpc, (dc, ac, oc, tdc)), (Up, lpp, (_, ap, _, _)) = sets_d[cur], sets_d[1 - cur]
+        for l in range(L):
+            bole.bole_commit_tree_verify(x.q[l], x.k[l], x.v[l], t.parent, x.g[l], x.beta[l],
+                                         pool[l], slot, t.tree_off, O[l], Uc[l], dc, ac, oc, tdc,
+                                         lpc[l], x.k[l], Up[l], lpp[l], ap, t.tree_off, accept,
+                                         rnd.err)
+
     def one_round(path):
+        if path == "deferred":  # two rounds, one on each buffer set
+            deferred_round(0)
+            deferred_round(1)
+            return
         verify_layers(path)
         commit()
 
+    one_round("tree")  # a real round in buffer set 0, copied to set 1
+    U2.copy_(U)
+    logP2.copy_(logP)
+    for a, b in zip(topo2, (t.depth, t.anc, t.order, t.tree_depth)):
+        a.copy_(b)
     for _ in range(max(args.warmup, 1)):
-        for p in ("tree", "fused"):
+        for p in ("tree", "fused", "deferred"):
             one_round(p)
     torch.cuda.synchronize()
     assert rnd.error_bits() == 0, "device error bits set"
     K = args.steps
-    graphs = {p: capture(torch, lambda p_=p: one_round(p_)) for p in ("tree", "fused")}
-    ms_round = {p: time_graphs([g], K, torch) for p, g in graphs.items()}
-    g_ver = capture(torch, lambda: verify_layers(args.path))
+    graphs = {p: capture(torch, lambda p_=p: one_round(p_)) for p in ("deferred", "tree", "fused")}
+    for g in graphs.values():  # untimed pre-roll
+        g.replay()
+    ms_round = {p: time_graphs([g], K, torch) / (2 if p == "deferred" else 1)
+                for p, g in graphs.items()}
+    g_ver = capture(torch, lambda: verify_layers("tree" if args.path == "deferred" else args.path))
     ms_verify = time_graphs([g_ver], max(K // 4, 5), torch)
     g_com = capture(torch, commit)
     ms_commit = time_graphs([g_com], max(K // 4, 5), torch)
     assert rnd.error_bits() == 0, "device error bits set"
 
     e = 2 if cfg.dtype == "bf16" else 4
-    dominant, bytes_fn = DOMINANT[args.path]
-    vbytes = bytes_fn(f.sizes(), H, cfg.d_k, cfg.d_v, e)
+    if args.path == "deferred":
+        dominant = "commit_tree_verify"
+        vbytes = commit_tree_verify_algorithmic_bytes(f.sizes(), f, H, cfg.d_k, cfg.d_v, e)
+        # per-layer launches of the deferred rounds, timed alone (graphs of two rounds)
+        g_dv = capture(torch, lambda: (deferred_round(0), deferred_round(1)))
+        ms_layer_deferred = time_graphs([g_dv], max(K // 4, 5), torch) / (2 * L)
+    else:
+        dominant, bytes_fn = DOMINANT[args.path]
+        vbytes = bytes_fn(f.sizes(), H, cfg.d_k, cfg.d_v, e)
     cbytes = commit_algorithmic_bytes(f, L, H, cfg.d_k, cfg.d_v, e)
     ms_layer = ms_verify / L
     step = ms_round[args.path]
+    ms_dom = ms_layer_deferred if args.path == "deferred" else ms_layer
     buckets = time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K)
-    achieved = vbytes / (ms_layer * 1e-3) / 1e9
+    achieved = vbytes / (ms_dom * 1e-3) / 1e9
     c_achieved = cbytes / (ms_commit * 1e-3) / 1e9
     out = {
         "metric": "tree nodes x heads verified/sec per GDN layer",
@@ -715,12 +753,15 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
             "workload": f"{cfg.name}: one round over L={L} layers, B={B} trees x T={cfg.T} nodes "
                         f"(random recursive, depth<={cfg.D}), H={H}, d_k=d_v={cfg.d_k}, "
                         f"{cfg.dtype} q/k/v, f32 gates and state; step = {L} x "
-                        f"{dominant} + one commit over all layers",
+                        + (f"{dominant} (each layer's verify with its commit of the previous "
+                           "round inside)" if args.path == "deferred"
+                           else f"{dominant} + one commit over all layers"),
             "L": L, "B": B, "T": cfg.T, "H": H, "d_k": cfg.d_k, "d_v": cfg.d_v, "nodes": N,
             "path": args.path,
             "timing": "HIP graph replays of whole rounds; verify and commit also alone",
             "ms_per_round": ms_round,
             "verify_ms_per_layer": ms_layer,
+            "commit_tree_verify_ms_per_layer": ms_dom if args.path == "deferred" else None,
             "commit_ms_per_round": ms_commit,
             "gc_bytes_per_round": {"tree/fused (on chip)": 0,
                                    "split: one workspace reused by every layer":
