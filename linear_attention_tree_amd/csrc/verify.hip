@@ -237,8 +237,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     // the Q/K rows go out now, in node order, behind wave 0's small loads;
     // the topology is derived while they stream in
     qk_issue<DT, true>(qkbuf, q, k, nullptr, T, off, H, h, d_k, 0);
-    // COMMIT: the path's key rows, right behind them
-    if (COMMIT) kpiece = pc.tile_load(threadIdx.x, 0, d_k);
+    // COMMIT: the path's key rows and the lane's U entries of its first 16
+    // positions, right behind them (they need only the path set, which came
+    // with the first scalar loads)
+    if (COMMIT) {
+      kpiece = pc.tile_load(threadIdx.x, 0, d_k);
+      pc.nodes(0, g4);
+      pc.load_u();
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (w == 0) {
       // tree preparation for this (tree, head): topology (tree_topo.h), then
@@ -298,13 +304,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     return;
   }
   if (COMMIT) {
-    // the lane's first 16 path positions and their U loads (the keys are
-    // staged in LDS with the Q/K rows)
+    // the weights of the lane's first 16 path positions (their U entries and
+    // key rows are in flight since the Q/K rows)
     pc.lpa = __shfl(pc.lp, pend ? pa : 0);
     pc.Pa = __builtin_bit_cast(
         float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, expf(pc.lpa))));
-    pc.nodes(0, g4);
-    pc.issue_u();
+    pc.weights();
   }
 
   // everything below depends on the rows only.  Issue order: the Q/K rows

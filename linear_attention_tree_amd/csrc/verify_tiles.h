@@ -150,13 +150,15 @@ struct PathCommit {
     const int left = La - kc_ - 4 * g4;
     return left >= 4 ? 15u : (left > 0 ? (1u << left) - 1u : 0u);
   }
-  // their weights, and the U loads (unconditional)
-  __device__ __forceinline__ void issue_u() {
+  // their U loads (unconditional)
+  __device__ __forceinline__ void load_u() {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wt[e] = expf(lpa - __shfl(lp, node[e]));
-      uraw[e] = up[(int64_t)node[e] * ustr + ucol];
-    }
+    for (int e = 0; e < 4; ++e) uraw[e] = up[(int64_t)node[e] * ustr + ucol];
+  }
+  // and their weights P_a / P_j
+  __device__ __forceinline__ void weights() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wt[e] = expf(lpa - __shfl(lp, node[e]));
   }
   // the step's B fragments: (P_a/P_j) U_j[v], split hi + lo
   __device__ __forceinline__ void bfrag(bool vin, int g4, bf16x4& bh, bf16x4& bl) const {
@@ -168,10 +170,12 @@ struct PathCommit {
                                            keep(vin && ((lm >> e) & 1u)));
     split_bf16x4(x, bh, bl);
   }
-  // A step's key rows are staged once per workgroup, transposed: kt[c][p] is
-  // key c of path position p (16 positions), so a lane's A fragment (four
-  // consecutive positions of one key) is one LDS read.  Thread t loads 8 bytes
-  // of position kc + t / 32 (unconditionally, a key past d_k reads key 0) and
+  // A step's key rows are staged once per workgroup, transposed: row c holds
+  // key c of the 16 path positions, so a lane's A fragment (four consecutive
+  // positions of one key) is one LDS read.  The four 4-position groups of row
+  // c are XOR-swizzled by (c / 8) % 4: the keys a read instruction touches in
+  // one 16-lane group then fall in distinct banks.  Thread t loads 8 bytes of
+  // position kc + t / 32 (unconditionally, a key past d_k reads key 0) and
   // writes them once they land.
   static constexpr int KPT = 8 / sizeof(KRaw);  // keys per thread
   using KPiece = std::conditional_t<DT == BOLE_BF16, u16x4, uint2>;
@@ -180,10 +184,13 @@ struct PathCommit {
     const int n = nth_set_bit(path, p < La ? p : 0);
     return *reinterpret_cast<const KPiece*>(kp + (int64_t)n * kstr + (c < d_k ? c : 0));
   }
+  static __device__ __forceinline__ int tile_at(int c, int p) {
+    return c * 16 + (p ^ (((c >> 3) & 3) << 2));
+  }
   __device__ __forceinline__ void tile_store(KRaw* kt, int t, const KPiece& v) const {
     const int p = t >> 5, c = KPT * (t & 31);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) kt[(c + i) * 16 + p] = v[i];
+    for (int i = 0; i < KPT; ++i) kt[tile_at(c + i, p)] = v[i];
   }
   // the whole tile for step kc, by every thread of the workgroup (uniform)
   __device__ __forceinline__ void stage(KRaw* kt, int kc, int d_k) const {
@@ -205,7 +212,7 @@ struct PathCommit {
       for (int half = 0; half < 2; ++half) {
         const int c = key(kk, half, l16);
         const uint32_t kok = keep(c < d_k);
-        const KVec kv = *reinterpret_cast<const KVec*>(kt + c * 16 + 4 * g4);
+        const KVec kv = *reinterpret_cast<const KVec*>(kt + tile_at(c, 4 * g4));
         bf16x4 ah, al;
         if (DT == BOLE_BF16) {
           u16x4 raw;
@@ -236,7 +243,8 @@ struct PathCommit {
     for (int kc = kc0; kc < La; kc += 16) {
       stage(kt, kc, d_k);
       nodes(kc, g4);
-      issue_u();
+      load_u();
+      weights();
       bf16x4 bh, bl;
       bfrag(vin, g4, bh, bl);
       apply(sx, 0, NK, kc == 0, bh, bl, l16, g4, d_k, kt);
