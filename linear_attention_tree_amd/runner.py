@@ -125,6 +125,30 @@ class TreeRound:
                               U, t.depth, t.anc, t.order, t.tree_depth, logP, self.err, stream)
         return O, U, logP
 
+    def commit_tree_layer(self, prev, prev_k, prev_U, prev_logP, prev_accept, q, k, v, log_gamma,
+                          beta, state_pool, slot, O=None, U=None, logP=None, stream=None):
+        """The previous round's commit of this layer, then this round's
+        tree_layer, in one launch (bole_commit_tree_verify).  prev is the
+        previous round's TreeRound (its topology), prev_k / prev_U / prev_logP
+        that round's keys, U and logP of this layer, prev_accept its accepted
+        nodes (-1: nothing to commit).  Request b must keep its slot between
+        the rounds.  Returns O, U and the layer's logP [N, H]."""
+        t, pt = self.topo, prev.topo
+        N, H, _ = q.shape
+        d_v = v.shape[2]
+        if O is None:
+            O = torch.empty(N, H, d_v, dtype=v.dtype, device=v.device)
+        if U is None:
+            U = torch.empty(N, H, d_v, dtype=torch.float32, device=v.device)
+        if logP is None:
+            logP = torch.empty(N, H, dtype=torch.float32, device=v.device)
+        prev_accept = torch.as_tensor(prev_accept, dtype=torch.int32).to(self.device)
+        bole.bole_commit_tree_verify(q, k, v, t.parent, log_gamma, beta, state_pool, slot,
+                                     t.tree_off, O, U, t.depth, t.anc, t.order, t.tree_depth, logP,
+                                     prev_k, prev_U, prev_logP, pt.anc, pt.tree_off, prev_accept,
+                                     self.err, stream)
+        return O, U, logP
+
     def commit(self, state_pool, slot, k, U, logP, accept, stream=None):
         t = self.topo
         accept = torch.as_tensor(accept, dtype=torch.int32).to(self.device)

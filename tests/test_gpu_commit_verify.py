@@ -213,3 +213,44 @@ def test_two_rounds_against_oracle(dtype):
     eu = block_rel_err(got["U"].cpu().numpy(), U2, f2.tree_off)
     say(f"  committed state {es:.2e}  O {eo:.2e}  U {eu:.2e} (bar {tol:g})")
     assert es <= tol and eo <= tol and eu <= tol
+
+
+def test_runner_commit_tree_layer():
+    """TreeRound.commit_tree_layer (the runner's form of the fused call) over
+    three rounds equals TreeRound.commit followed by tree_layer, bit for bit."""
+    from linear_attention_tree_amd import TreeRound
+    cfg = cfg_of("cv_runner", 64, B=3, H=2)
+    forests = [W.make_forest(cfg, 20 + r) for r in range(3)]
+    xs = [W.make_layer(cfg, len(f.parent), 0, 20 + r) for r, f in enumerate(forests)]
+    n_slots = cfg.B + 1
+    slot_np = np.array([2, 0, 3], np.int32)
+    pool0 = prefix_slots(cfg, 0, n_slots, slot_np, 20)
+    slot = torch.from_numpy(slot_np).cuda()
+    outs = {}
+    for mode in ("fused", "two_calls"):
+        pool = torch.from_numpy(pool0).cuda()
+        prev = None
+        res = []
+        for f, x in zip(forests, xs):
+            r = device_round(cfg, f, x)
+            rnd = TreeRound(f.parent, f.tree_off, cfg.H)
+            if prev is None:
+                O, U, lp = rnd.tree_layer(r["q"], r["k"], r["v"], r["g"], r["beta"], pool, slot)
+            elif mode == "fused":
+                p_rnd, p_r, p_U, p_lp, p_acc = prev
+                O, U, lp = rnd.commit_tree_layer(p_rnd, p_r["k"], p_U, p_lp, p_acc, r["q"], r["k"],
+                                                 r["v"], r["g"], r["beta"], pool, slot)
+            else:
+                p_rnd, p_r, p_U, p_lp, p_acc = prev
+                p_rnd.commit(pool, slot, p_r["k"], p_U, p_lp, p_acc)
+                O, U, lp = rnd.tree_layer(r["q"], r["k"], r["v"], r["g"], r["beta"], pool, slot)
+            prev = (rnd, r, U, lp, f.accept)
+            torch.cuda.synchronize()
+            assert rnd.error_bits() == 0
+            res.append((O.view(torch.int16).clone(), U.view(torch.int32).clone()))
+        res.append(pool.view(torch.int32).clone())
+        outs[mode] = res
+    say("runner commit_tree_layer: three rounds")
+    for a, b in zip(outs["fused"][:-1], outs["two_calls"][:-1]):
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(outs["fused"][-1], outs["two_calls"][-1])
