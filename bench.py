@@ -624,14 +624,42 @@ def time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K):
     out = {}
     for c in buckets:
         br.accept.copy_(torch.from_numpy((sizes[c] - 1).astype(np.int32)))
-        ms = time_graphs([br.graphs[c]], max(K // 4, 5), torch)
+        ms = time_graphs([br.graphs[(c, 0)]], max(K // 4, 5), torch)
         out[str(c)] = {"ms_per_round": ms, "nodes": int(sizes[c].sum()),
                        "node_heads_per_s": float(sizes[c].sum()) * cfg.H * L / (ms * 1e-3)}
     assert int(br.err.item()) == 0, "device error bits set"
+    del br
+    # the same rounds with each layer's launch carrying its commit of the
+    # previous round (graphs of the two parities replayed in turn; each round
+    # commits the previous round's accepted nodes of the same bucket)
+    bd = BucketedRound(B, L, cfg.H, cfg.d_k, cfg.d_v, x.v.dtype, int(cands.cand_off[-1]), buckets,
+                       device=dev, deferred=True)
+    for par in (0, 1):
+        for name in ("q", "k", "v", "g", "beta"):
+            bd.tokens(par)[name].copy_(getattr(x, name))
+    bd.cand_parent.copy_(torch.from_numpy(cands.cand_parent))
+    bd.p_draft.copy_(torch.from_numpy(cands.p_draft))
+    bd.cand_off.copy_(torch.from_numpy(cands.cand_off))
+    bd.accept.fill_(-1)
+    pool_d = pool.clone()
+    bd.capture(pool_d, slot)
+    out_d = {}
+    for c in buckets:
+        bd.accept.fill_(-1)  # the first round of this bucket commits nothing
+        bd.graphs[(c, 0)].replay()
+        bd.accept.copy_(torch.from_numpy((sizes[c] - 1).astype(np.int32)))
+        bd.graphs[(c, 1)].replay()  # from here each round commits the previous one
+        ms = time_graphs([bd.graphs[(c, 0)], bd.graphs[(c, 1)]], 2 * max(K // 8, 3), torch)
+        out_d[str(c)] = {"ms_per_round": ms, "nodes": int(sizes[c].sum()),
+                         "node_heads_per_s": float(sizes[c].sum()) * cfg.H * L / (ms * 1e-3)}
+    assert int(bd.err.item()) == 0, "device error bits set"
     return {"note": "per capacity bucket: bole_forest_build over drafted candidates "
                     f"({int(cands.cand_off[-1])} for {B} requests), {L} x bole_tree_verify, one "
                     "bole_commit_path; one captured graph per bucket",
-            "by_capacity": out}
+            "by_capacity": out,
+            "deferred_note": f"the same with {L} x bole_commit_tree_verify (each layer carries "
+                             "its commit of the previous round) and no commit launch",
+            "deferred_by_capacity": out_d}
 
 
 def round_main(cfg, args, torch, TreeRound, bole, dev):

@@ -210,27 +210,45 @@ class BucketedRound:
     `capacity` rows of each layer) and its accepted nodes into the input
     buffers and replays the graph of the smallest bucket whose capacity holds
     its budget.  The verify grid does not depend on the node count, so one
-    bucket's graph serves every forest up to its capacity."""
+    bucket's graph serves every forest up to its capacity.
+
+    deferred=True: each layer's launch carries that layer's commit of the
+    previous round (bole_commit_tree_verify) and there is no commit launch.
+    Rounds alternate between two sets of token, U and logP buffers (`parity`,
+    flipped by every replay; the caller fills the token buffers of the parity
+    about to run, `tokens()`), and each round keeps its forest offsets and
+    ancestor sets for the next.  `accept` holds the previous round's accepted
+    nodes when a round runs (-1 for nothing to commit: set it so before the
+    first round and before capture)."""
 
     def __init__(self, B: int, L: int, H: int, d_k: int, d_v: int, dtype: torch.dtype,
-                 M_total: int, buckets, max_tree: int = bole.MAX_TREE, device="cuda"):
+                 M_total: int, buckets, max_tree: int = bole.MAX_TREE, device="cuda",
+                 deferred: bool = False):
         dev = torch.device(device)
         i32, f32 = torch.int32, torch.float32
         self.B, self.L, self.H = B, L, H
+        self.deferred = deferred
         self.buckets = sorted(int(c) for c in buckets)
         cmax = self.buckets[-1]
         self.cand_parent = torch.zeros(M_total, dtype=i32, device=dev)
         self.p_draft = torch.zeros(M_total, dtype=f32, device=dev)
         self.cand_off = torch.zeros(B + 1, dtype=i32, device=dev)
-        self.q = torch.zeros(L, cmax, H, d_k, dtype=dtype, device=dev)
-        self.k = torch.zeros_like(self.q)
-        self.v = torch.zeros(L, cmax, H, d_v, dtype=dtype, device=dev)
-        self.g = torch.zeros(L, cmax, H, dtype=f32, device=dev)
-        self.beta = torch.zeros(L, cmax, H, dtype=f32, device=dev)
+
+        def token_set():
+            return dict(q=torch.zeros(L, cmax, H, d_k, dtype=dtype, device=dev),
+                        k=torch.zeros(L, cmax, H, d_k, dtype=dtype, device=dev),
+                        v=torch.zeros(L, cmax, H, d_v, dtype=dtype, device=dev),
+                        g=torch.zeros(L, cmax, H, dtype=f32, device=dev),
+                        beta=torch.zeros(L, cmax, H, dtype=f32, device=dev),
+                        U=torch.zeros(L, cmax, H, d_v, dtype=f32, device=dev),
+                        logP=torch.zeros(L, cmax, H, dtype=f32, device=dev),
+                        anc=torch.zeros(cmax, dtype=torch.int64, device=dev),
+                        tree_off=torch.zeros(B + 1, dtype=i32, device=dev))
+
+        self.sets = [token_set()] + ([token_set()] if deferred else [])
+        self.parity = 0
         self.accept = torch.zeros(B, dtype=i32, device=dev)
         self.O = torch.zeros(L, cmax, H, d_v, dtype=dtype, device=dev)
-        self.U = torch.zeros(L, cmax, H, d_v, dtype=f32, device=dev)
-        self.logP = torch.zeros(L, cmax, H, dtype=f32, device=dev)
         self.err = torch.zeros(1, dtype=i32, device=dev)
         self.forest = {c: ForestBuilder(B, M_total, c, max_tree, dev, self.err)
                        for c in self.buckets}
@@ -242,36 +260,67 @@ class BucketedRound:
                      for c in self.buckets}
         self.graphs = {}
 
+    # the current parity's buffers (the only set without deferred)
+    def tokens(self, parity: Optional[int] = None) -> dict:
+        return self.sets[self.parity if parity is None else parity]
+
+    q = property(lambda self: self.tokens()["q"])
+    k = property(lambda self: self.tokens()["k"])
+    v = property(lambda self: self.tokens()["v"])
+    g = property(lambda self: self.tokens()["g"])
+    beta = property(lambda self: self.tokens()["beta"])
+    U = property(lambda self: self.tokens()["U"])
+    logP = property(lambda self: self.tokens()["logP"])
+
     def bucket(self, budget: int) -> int:
         for c in self.buckets:
             if budget <= c:
                 return c
         raise ValueError(f"budget {budget} exceeds the largest bucket {self.buckets[-1]}")
 
-    def run_eager(self, capacity: int, state_pool, slot, commit=True):
+    def run_eager(self, capacity: int, state_pool, slot, commit=True, parity=None):
         """One round launched call by call (what the graph of `capacity` holds)."""
         fb, t, c = self.forest[capacity], self.topo[capacity], capacity
+        par = self.parity if parity is None else parity
+        cur = self.sets[par]
         fb.build(self.cand_parent, self.p_draft, self.cand_off)
+        if self.deferred:
+            prev = self.sets[1 - par]
+            for l in range(self.L):
+                bole.bole_commit_tree_verify(
+                    cur["q"][l, :c], cur["k"][l, :c], cur["v"][l, :c], fb.parent,
+                    cur["g"][l, :c], cur["beta"][l, :c], state_pool[l], slot, fb.tree_off,
+                    self.O[l, :c], cur["U"][l, :c], t.depth, t.anc, t.order, t.tree_depth,
+                    cur["logP"][l, :c], prev["k"][l], prev["U"][l], prev["logP"][l], prev["anc"],
+                    prev["tree_off"], self.accept, self.err)
+            # this round's forest, kept for the next round's commits
+            cur["anc"][:c].copy_(t.anc)
+            cur["tree_off"].copy_(fb.tree_off)
+            return
         for l in range(self.L):
-            bole.bole_tree_verify(self.q[l, :c], self.k[l, :c], self.v[l, :c], fb.parent,
-                                  self.g[l, :c], self.beta[l, :c], state_pool[l], slot,
-                                  fb.tree_off, self.O[l, :c], self.U[l, :c], t.depth, t.anc,
-                                  t.order, t.tree_depth, self.logP[l, :c], self.err)
+            bole.bole_tree_verify(cur["q"][l, :c], cur["k"][l, :c], cur["v"][l, :c], fb.parent,
+                                  cur["g"][l, :c], cur["beta"][l, :c], state_pool[l], slot,
+                                  fb.tree_off, self.O[l, :c], cur["U"][l, :c], t.depth, t.anc,
+                                  t.order, t.tree_depth, cur["logP"][l, :c], self.err)
         if commit:
-            bole.bole_commit_path(state_pool, slot, self.k[:, :c], self.U[:, :c],
-                                  self.logP[:, :c], t.anc, fb.tree_off, self.accept, self.err)
+            bole.bole_commit_path(state_pool, slot, cur["k"][:, :c], cur["U"][:, :c],
+                                  cur["logP"][:, :c], t.anc, fb.tree_off, self.accept, self.err)
 
     def capture(self, state_pool, slot, commit=True):
-        """Capture every bucket's round against these state-pool and slot
-        buffers (they too must keep their addresses).  The uncaptured pass that
-        precedes each capture runs the round once, commit included, on the
-        inputs loaded now: load a valid round first (empty candidate sets give
-        empty trees, which the verify calls report)."""
+        """Capture every bucket's round (and with deferred, both parities)
+        against these state-pool and slot buffers (they too must keep their
+        addresses).  The uncaptured pass that precedes each capture runs the
+        round once, commits included, on the inputs loaded now: load a valid
+        round first (empty candidate sets give empty trees, which the verify
+        calls report), and with deferred set `accept` to -1."""
         for c in self.buckets:
-            self.graphs[c] = capture_graph(
-                lambda c_=c: self.run_eager(c_, state_pool, slot, commit))
+            for par in range(len(self.sets)):
+                self.graphs[(c, par)] = capture_graph(
+                    lambda c_=c, p_=par: self.run_eager(c_, state_pool, slot, commit, p_))
 
     def replay(self, budget: int) -> int:
         c = self.bucket(budget)
-        self.graphs[c].replay()
+        self.graphs[(c, self.parity)].replay()
+        if self.deferred:
+            self.parity ^= 1
         return c
