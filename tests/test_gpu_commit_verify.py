@@ -254,3 +254,31 @@ def test_runner_commit_tree_layer():
     for a, b in zip(outs["fused"][:-1], outs["two_calls"][:-1]):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert torch.equal(outs["fused"][-1], outs["two_calls"][-1])
+
+
+def test_target_shape():
+    """The headline shape (16 trees x 64 nodes, 32 heads, d = 128, bf16) in
+    the launch configuration the bench times: against the two calls bit for
+    bit, and eight sampled (request, head) units against the fp64 oracle over
+    both rounds."""
+    cfg = W.CONFIGS["target"]
+    f1, x1, f2, x2, pool0, slot, acc = two_rounds(cfg, 30)
+    say(f"commit+verify target shape, N1={len(f1.parent)} N2={len(f2.parent)}")
+    got, want = run_pair(cfg, f1, x1, f2, x2, pool0, slot, acc)
+    assert got["err"] == 0
+    assert_same(got, want)
+    rng = np.random.default_rng(31)
+    units = [(int(b), int(h)) for b, h in zip(rng.integers(0, cfg.B, 8), rng.integers(0, cfg.H, 8))]
+    _, _, S1 = oracle.verify(f1.parent, f1.tree_off, x1.q64, x1.k64, x1.v64, x1.g64, x1.beta64,
+                             pool0, slot, acc, units)
+    pool1 = pool0.astype(np.float64)
+    for b, h in units:
+        pool1[slot[b], h] = S1[b, h]
+    O2, U2, _ = oracle.verify(f2.parent, f2.tree_off, x2.q64, x2.k64, x2.v64, x2.g64, x2.beta64,
+                              pool1, slot, None, units)
+    tol = tolerance(cfg)
+    es = state_rel_err(got["pool"].cpu().numpy(), S1, slot, units)
+    eo = block_rel_err(got["O"].float().cpu().numpy(), O2, f2.tree_off, units)
+    eu = block_rel_err(got["U"].cpu().numpy(), U2, f2.tree_off, units)
+    say(f"  sampled units {units}: committed state {es:.2e}  O {eo:.2e}  U {eu:.2e}")
+    assert es <= tol and eo <= tol and eu <= tol
