@@ -92,9 +92,16 @@ DOMINANT = {  # path -> (launch name, algorithmic bytes of one launch)
 
 
 def kernel_source_hash():
+    """Hash of the dominant kernel's sources with comments and blank lines
+    left out (a comment edit does not change the kernel the counters saw)."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

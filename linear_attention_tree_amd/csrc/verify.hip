@@ -31,6 +31,12 @@
 //           leave as 4-element pieces of the nodes' rows; V arrives the same
 //           way, as 16-byte row pieces staged for the accumulator layout.
 //
+// COMMIT (bole_commit_tree_verify): before phase A reads the state, the
+// previous round's accepted path is committed into it (paper Eq. 10) in the
+// lane's registers, with bole_commit_path's MFMA steps on the same operands
+// (PathCommit), and the committed rows are written back to the slot; the
+// verify then uses them as S_pre.
+//
 // Two other exact solves can be selected (SOLVE):
 //  Neumann  the d_b-step propagation of Eq. 8 as the pages run it: Z <- -G Z,
 //           U += Z, starting from Z = U = R.  Z^(m) = (-G)^m R vanishes on rows
