@@ -2,9 +2,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 tree preparation (topology + log-space gate products), the G/C factors,
-value-tiled verify and the accepted-path commit.  The default path runs the
-first three in one launch (bole_tree_verify), then the commit; --path fused
-and --path split time the three- and four-launch forms.  Default workload: 16 requests,
+value-tiled verify and the accepted-path commit.  The default path runs all
+of it in one launch (bole_commit_tree_verify: this round's preparation,
+factors and verify with the previous round's commit inside); --path tree
+times bole_tree_verify + bole_commit_path, and --path fused and --path split
+the three- and four-launch forms.  Default workload: 16 requests,
 64-node random trees (depth <= 12), 32 state heads, d_k = d_v = 128, bf16
 q/k/v with float32 gates and states.  Several independent input sets are
 rotated so the bytes touched per rotation exceed the 256 MB last-level cache.
