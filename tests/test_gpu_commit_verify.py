@@ -79,9 +79,10 @@ def outputs(r, pool):
                 err=int(r["err"].item()))
 
 
-def run_pair(cfg, f1, x1, f2, x2, pool0, slot_np, accept1):
+def run_pair(cfg, f1, x1, f2, x2, pool0, slot_np, accept1, prev_off=None):
     """Round one by bole_tree_verify; then round two both ways: the reference
-    (bole_commit_path of round one, then bole_tree_verify) and the fused call."""
+    (bole_commit_path of round one, then bole_tree_verify) and the fused call.
+    prev_off replaces round one's offsets in both commits (bad ranges)."""
     from linear_attention_tree_amd import bole
     slot = torch.from_numpy(slot_np).cuda()
     acc = torch.from_numpy(np.asarray(accept1, np.int32)).cuda()
@@ -90,9 +91,10 @@ def run_pair(cfg, f1, x1, f2, x2, pool0, slot_np, accept1):
     torch.cuda.synchronize()
     assert int(r1["err"].item()) == 0
 
+    p_off = r1["tree_off"] if prev_off is None else torch.from_numpy(prev_off).cuda()
     ref2 = device_round(cfg, f2, x2)
     pool_a = torch.from_numpy(pool0).cuda()
-    bole.bole_commit_path(pool_a, slot, r1["k"], r1["U"], r1["logP"], r1["anc"], r1["tree_off"],
+    bole.bole_commit_path(pool_a, slot, r1["k"], r1["U"], r1["logP"], r1["anc"], p_off,
                           acc, ref2["err"])
     tree_verify(ref2, pool_a, slot)
     want = outputs(ref2, pool_a)
@@ -103,7 +105,7 @@ def run_pair(cfg, f1, x1, f2, x2, pool0, slot_np, accept1):
         fus2["q"], fus2["k"], fus2["v"], fus2["parent"], fus2["g"], fus2["beta"], pool_b, slot,
         fus2["tree_off"], fus2["O"], fus2["U"], fus2["depth"], fus2["anc"], fus2["order"],
         fus2["tree_depth"], fus2["logP"], r1["k"], r1["U"], r1["logP"], r1["anc"],
-        r1["tree_off"], acc, fus2["err"])
+        p_off, acc, fus2["err"])
     got = outputs(fus2, pool_b)
     return got, want
 
@@ -282,3 +284,26 @@ def test_target_shape():
     eu = block_rel_err(got["U"].cpu().numpy(), U2, f2.tree_off, units)
     say(f"  sampled units {units}: committed state {es:.2e}  O {eo:.2e}  U {eu:.2e}")
     assert es <= tol and eo <= tol and eu <= tol
+
+
+def test_bad_previous_ranges():
+    """Previous ranges that are empty, longer than 64 nodes or past the previous
+    forest: TREE_SIZE, no commit for those requests, the others committed."""
+    cfg = cfg_of("cv_badprev", 65, B=4, H=2)
+    f1, x1, f2, x2, pool0, slot, acc = two_rounds(cfg, 16)
+    n1 = len(f1.parent)
+    off = f1.tree_off.astype(np.int32).copy()
+    off[1] = off[0]            # request 0: empty
+    off[2] = off[1] + 65       # request 1: 65 nodes
+    off[3] = off[2] + 10       # request 2: 10 nodes (committed)
+    off[4] = n1 + 5            # request 3: past the end of the previous forest
+    acc = np.zeros(cfg.B, np.int32)
+    say(f"commit+verify bad previous ranges {off.tolist()}")
+    got, want = run_pair(cfg, f1, x1, f2, x2, pool0, slot, acc, prev_off=off)
+    from linear_attention_tree_amd import bole
+    assert got["err"] == want["err"] == bole.ERR_TREE_SIZE, (got["err"], want["err"])
+    assert_same(got, want)
+    for b, changed in ((0, False), (1, False), (2, True), (3, False)):
+        same = np.array_equal(got["pool"][slot[b]].cpu().numpy().view(np.uint32),
+                              pool0[slot[b]].view(np.uint32))
+        assert same != changed, b
