@@ -12,7 +12,8 @@
 //     rho bits (63..32) | 1023 - depth (31..22) | 4095 - request (21..10)
 //       | 1023 - candidate (9..0),
 // larger first: rho descending, then depth, request and candidate ascending.
-// For rho >= 0 the float's bits order like its value, and the key is unique.
+// For rho >= 0 the float's bits order like its value (a -0.0 score enters the
+// key as +0.0), and the key is unique.
 //
 // Two launches.  forest_score_kernel, one workgroup per request: validation,
 // depth and rho level by level, the key, and each candidate's rank within its
@@ -36,8 +37,13 @@ constexpr int kMaxListed = 16384;                   // B * max_tree
 constexpr int kListPer = kMaxListed / kPackThreads;  // listed keys per packing thread
 constexpr int kWalk = 16;  // path length a node collects in registers
 
+// A probability of -0.0 passes validation (it compares equal to 0) and makes
+// rho -0.0, whose sign bit would put its raw bits above every positive score:
+// the key takes rho's value, so both zeros rank as +0.0 (then by depth).  The
+// rho reported to the caller keeps the product's own bits.
 __device__ __forceinline__ uint64_t cand_key(float rho, int depth, int b, int i) {
-  return ((uint64_t)__float_as_uint(rho) << 32) | ((uint64_t)(1023 - depth) << 22) |
+  const uint32_t score = rho == 0.0f ? 0u : __float_as_uint(rho);
+  return ((uint64_t)score << 32) | ((uint64_t)(1023 - depth) << 22) |
          ((uint64_t)(4095 - b) << 10) | (uint64_t)(1023 - i);
 }
 

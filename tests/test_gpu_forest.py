@@ -101,6 +101,37 @@ def test_forest_large_trees_ties_and_zeros():
                     OF.build_forest(par, p, off, capacity, max_tree))
 
 
+def test_forest_negative_zero_probabilities():
+    """A draft probability of -0.0 is a valid zero: its score ranks as +0.0 (then
+    by depth), below every positive score, while the reported rho keeps the
+    product's sign bit.  At a root (so the whole tree scores -0.0, and a -0.0
+    child of it +0.0), at inner nodes, and beside ordinary requests; bit-exact
+    against the oracle, at capacities that cut through the zero scores."""
+    nz = np.float32(-0.0)
+    trees = [
+        (np.array([-1, 0, 0], np.int32), np.array([1.0, nz, 0.5], np.float32)),
+        (np.array([-1, 0, 1, 0, 3], np.int32), np.array([nz, 1.0, 0.5, nz, 0.25], np.float32)),
+        (np.array([-1, 0, 0, 1, 2, 2], np.int32),
+         np.array([1.0, 0.75, nz, nz, 0.0, 0.5], np.float32)),
+    ]
+    good = W.make_candidates(2, seed=11)
+    par = np.concatenate([t[0] for t in trees] + [good.cand_parent]).astype(np.int32)
+    p = np.concatenate([t[1] for t in trees] + [good.p_draft]).astype(np.float32)
+    off = np.concatenate([[0], np.cumsum([len(t[0]) for t in trees]),
+                          sum(len(t[0]) for t in trees) + good.cand_off[1:]]).astype(np.int32)
+    for capacity in (2, 4, 8, 12, 40, len(par)):
+        for max_tree in (2, 64):
+            say(f"forest -0.0: capacity={capacity} max_tree={max_tree}")
+            out = gpu_build(par, p, off, capacity, max_tree)
+            ref = OF.build_forest(par, p, off, capacity, max_tree)
+            assert ref["err"] == 0
+            assert_same(out, ref)
+    # the smallest case on its own: the -0.0 child does not outrank its root
+    out = gpu_build(trees[0][0], trees[0][1], np.array([0, 3], np.int32), 2, 64)
+    assert out["err"] == 0
+    assert out["cand_of"].tolist() == [0, 2] and out["parent"].tolist() == [-1, 0]
+
+
 @pytest.mark.parametrize("bad,bits", [
     (([-1, 0, 7], [1.0, 0.5, 0.5]), OF.ERR_BAD_PARENT),
     (([-1, 1, 1], [1.0, 0.5, 0.5]), OF.ERR_BAD_PARENT),

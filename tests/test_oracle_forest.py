@@ -124,6 +124,24 @@ def test_equal_scores_fall_to_depth():
         assert out["cand_of"][:capacity].tolist() == want
 
 
+def test_negative_zero_is_a_zero_score():
+    """p = -0.0 is a probability of zero: it scores like +0.0, so it ranks below
+    every positive score, ties with other zeros fall to depth, and the selection
+    stays prefix-closed (the -0.0 child never precedes its root).  The reported
+    rho keeps the float32 product's sign."""
+    nz = np.float32(-0.0)
+    par = np.array([-1, 0, 0], np.int32)
+    out = F.build_forest(par, np.array([1.0, nz, 0.5], np.float32), np.array([0, 3]), 2, 64)
+    assert out["cand_of"].tolist() == [0, 2] and out["parent"].tolist() == [-1, 0]
+    assert np.signbit(out["rho"][1]) and out["rho"][1] == 0.0
+    # a -0.0 root: every score is zero, taken level by level (depth, then index)
+    par = np.array([-1, 0, 1, 0], np.int32)
+    p = np.array([nz, 1.0, 0.5, nz], np.float32)
+    out = F.build_forest(par, p, np.array([0, 4]), 3, 64)
+    assert out["cand_of"].tolist() == [0, 1, 3] and out["parent"].tolist() == [-1, 0, 0]
+    assert out["rho"].view(np.uint32).tolist() == [0x80000000, 0x80000000, 0x80000000, 0]
+
+
 @pytest.mark.parametrize("bad,bits", [
     (([-1, 0, 7], [1.0, 0.5, 0.5]), F.ERR_BAD_PARENT),
     (([-1, 1, 1], [1.0, 0.5, 0.5]), F.ERR_BAD_PARENT),
