@@ -78,6 +78,15 @@ def block_rel_err(x: np.ndarray, ref: np.ndarray, tree_off: np.ndarray, units=No
     ref = np.asarray(ref, np.float64)
     B = len(tree_off) - 1
     H = ref.shape[1]
+    starts = np.asarray(tree_off[:-1], np.int64)
+    if units is None and B > 0 and np.all(np.diff(tree_off) > 0) and tree_off[-1] == len(ref):
+        # every block at once: per-row maxima over d, then per-tree maxima
+        d = np.maximum.reduceat(np.max(np.abs(x - ref), axis=2), starts, axis=0)
+        den = np.maximum.reduceat(np.max(np.abs(ref), axis=2), starts, axis=0)
+        rel = np.where(den > 0, d / np.where(den > 0, den, 1.0), d)
+        if np.isnan(rel).any():
+            return float("nan")
+        return float(np.max(rel))
     todo = units if units is not None else [(b, h) for b in range(B) for h in range(H)]
     worst = 0.0
     for b, h in todo:
@@ -89,6 +98,15 @@ def block_rel_err(x: np.ndarray, ref: np.ndarray, tree_off: np.ndarray, units=No
 
 
 def state_rel_err(S_gpu: np.ndarray, S_ref: np.ndarray, slot, units) -> float:
+    """max over the listed (request, head) units of max|S - ref| / max|ref| over
+    the unit's d_v x d_k state; S_gpu is a slot pool, S_ref per request."""
+    if len(set(units)) == len(slot) * S_ref.shape[1]:  # every unit at once
+        a = np.asarray(S_gpu[np.asarray(slot)], np.float64)
+        r = np.asarray(S_ref, np.float64)
+        d = np.max(np.abs(a - r), axis=(2, 3))
+        den = np.maximum(np.max(np.abs(r), axis=(2, 3)), 1e-300)
+        out = d / den
+        return float("nan") if np.isnan(out).any() else float(np.max(out))
     worst = 0.0
     for b, h in units:
         a = np.asarray(S_gpu[slot[b], h], np.float64)

@@ -268,6 +268,22 @@ def make_prefix(cfg: Config, layer: int, b: int, h: int, seed: int = 0) -> Prefi
                         beta64=beta.astype(np.float32).astype(np.float64))
 
 
+# Spread of the committed states the prefix recipe produces (256 prefix tokens
+# of the default gates from a zero state: entries with standard deviation
+# about 0.06, largest magnitudes about 0.6).
+STATE_STD = 0.06
+
+
+def make_states(cfg: Config, n_slots: int, layer: int = 0, seed: int = 0,
+                std: float = STATE_STD) -> np.ndarray:
+    """Committed states drawn directly, [n_slots, H, d_v, d_k] float32 with
+    N(0, std^2) entries: a stand-in for prefix-built states where running the
+    recurrence over every prefix would dominate a large case."""
+    rng = _rng(seed, cfg, STREAM_PREFIX, layer, 1 << 22)
+    return (rng.standard_normal((n_slots, cfg.H, cfg.d_v, cfg.d_k), dtype=np.float32)
+            * np.float32(std))
+
+
 def chain_forest(B: int, T: int) -> Forest:
     """B chains of T nodes each (node i's parent is i-1)."""
     one = np.arange(-1, T - 1, dtype=np.int32)
