@@ -36,8 +36,9 @@
  *    per-node gates [N, H].  Committed states use the serving slot layout
  *    [slot, H, d_v, d_k] (arXiv page, state-lifecycle paragraph), float32.
  *  - d_k and d_v are multiples of 16 in [16, 256].
- *  - Stateless and reentrant: no global state; calls on different streams may
- *    overlap as long as they do not write the same buffers.
+ *  - Stateless and reentrant: no global state (the one exception is the
+ *    per-GPU scratch array of bole_forest_build_noalloc); calls on different
+ *    streams may overlap as long as they do not write the same buffers.
  */
 #ifndef BOLE_H
 #define BOLE_H
@@ -430,6 +431,30 @@ BOLE_API int bole_forest_build(const int32_t* cand_parent, const float* p_draft,
                                int32_t capacity, int32_t max_tree, float* rho, int32_t* parent,
                                int32_t* cand_of, int32_t* tree_off, void* workspace,
                                uint32_t* err, void* stream);
+
+/*
+ * bole_forest_build_noalloc - bole_forest_build for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same selection, packing, outputs and
+ * error bits, bit for bit, from the same kernels; the workspace is a fixed
+ * device array inside the library (192 KiB per GPU, held until the process
+ * ends) instead of an argument.  Nothing is allocated or freed: the array's
+ * device address is looked up once per GPU, on the first call made with that
+ * GPU current.
+ *
+ *  arguments, outputs and errors as bole_forest_build, without `workspace`.
+ *  Limits as bole_forest_build (B * max_tree <= 16384 is exactly the array's
+ *  capacity); BOLE_E_SHAPE beyond them, BOLE_E_HIP if the runtime cannot
+ *  name the current device or the array's address.
+ * Every call on one GPU uses that GPU's single array: calls that overlap on
+ * one GPU (concurrent streams, or host threads) race and must be serialised
+ * by the caller.  `stream` must belong to the current device.
+ */
+BOLE_API int bole_forest_build_noalloc(const int32_t* cand_parent, const float* p_draft,
+                                       const int32_t* cand_off, int32_t B, int32_t M_total,
+                                       int32_t capacity, int32_t max_tree, float* rho,
+                                       int32_t* parent, int32_t* cand_of, int32_t* tree_off,
+                                       uint32_t* err, void* stream);
 
 /* Static description of a bole_status code. */
 BOLE_API const char* bole_status_string(int code);

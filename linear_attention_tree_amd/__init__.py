@@ -11,7 +11,7 @@ from .bole import (  # noqa: F401
     ERR_TREE_SIZE, MAX_TREE, BoleError, bole_commit_path, bole_factor_gc, bole_factor_verify,
     bole_conv_commit, bole_gc_workspace_bytes, bole_status_string, bole_tree_conv, bole_tree_prep,
     bole_tree_verify, bole_commit_tree_verify, bole_verify, bole_verify_neumann, bole_factor_inverse, bole_verify_inverse,
-    bole_forest_build, bole_forest_workspace_bytes, lib,
+    bole_forest_build, bole_forest_build_noalloc, bole_forest_workspace_bytes, lib,
 )
 from .runner import BucketedRound, ForestBuilder, Topology, TreeRound  # noqa: F401
 
@@ -19,6 +19,7 @@ __all__ = [
     "bole_tree_prep", "bole_factor_gc", "bole_verify", "bole_factor_verify", "bole_tree_verify",
     "bole_commit_tree_verify", "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
     "bole_commit_path", "bole_tree_conv", "bole_conv_commit", "bole_forest_build",
+    "bole_forest_build_noalloc",
     "bole_forest_workspace_bytes", "ForestBuilder", "BucketedRound",
     "bole_gc_workspace_bytes", "bole_status_string", "BoleError", "TreeRound", "Topology", "lib",
 ]

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.bole_forest_workspace_bytes.argtypes = [i32, i32]
         L.bole_forest_build.restype = ctypes.c_int
         L.bole_forest_build.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.bole_forest_build_noalloc.restype = ctypes.c_int
+        L.bole_forest_build_noalloc.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P]
         L.bole_status_string.restype = ctypes.c_char_p
         L.bole_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -508,13 +510,7 @@ def bole_forest_workspace_bytes(B: int, max_tree: int) -> int:
     return int(lib().bole_forest_workspace_bytes(B, max_tree))
 
 
-def bole_forest_build(cand_parent, p_draft, cand_off, capacity, max_tree, rho, parent, cand_of,
-                      tree_off, workspace, err=None, stream=None):
-    """Budget selection by cumulative draft probability and the packed forest
-    (see bole.h).  cand_parent [M_total] int32, p_draft [M_total] float32,
-    cand_off [B+1] int32; outputs rho [M_total] float32, parent and cand_of
-    [capacity] int32, tree_off [B+1] int32; workspace uint8 of at least
-    bole_forest_workspace_bytes(B, max_tree) bytes."""
+def _forest_args(cand_parent, p_draft, cand_off, capacity, rho, parent, cand_of, tree_off, err):
     _need(cand_parent, "cand_parent", torch.int32, 1)
     _need(p_draft, "p_draft", torch.float32, 1)
     _need(cand_off, "cand_off", torch.int32, 1)
@@ -532,11 +528,35 @@ def bole_forest_build(cand_parent, p_draft, cand_off, capacity, max_tree, rho, p
     _need(tree_off, "tree_off", torch.int32, 1)
     if tree_off.shape[0] != B + 1:
         raise ValueError("tree_off needs B + 1 entries")
+    _need(err, "err", torch.int32, 1, allow_none=True)
+    return B, M_total
+
+
+def bole_forest_build(cand_parent, p_draft, cand_off, capacity, max_tree, rho, parent, cand_of,
+                      tree_off, workspace, err=None, stream=None):
+    """Budget selection by cumulative draft probability and the packed forest
+    (see bole.h).  cand_parent [M_total] int32, p_draft [M_total] float32,
+    cand_off [B+1] int32; outputs rho [M_total] float32, parent and cand_of
+    [capacity] int32, tree_off [B+1] int32; workspace uint8 of at least
+    bole_forest_workspace_bytes(B, max_tree) bytes."""
+    B, M_total = _forest_args(cand_parent, p_draft, cand_off, capacity, rho, parent, cand_of,
+                              tree_off, err)
     _need(workspace, "workspace", torch.uint8, 1)
     if workspace.numel() < bole_forest_workspace_bytes(B, max_tree):
         raise ValueError("workspace too small")
-    _need(err, "err", torch.int32, 1, allow_none=True)
     _check("bole_forest_build", lib().bole_forest_build(
         _ptr(cand_parent), _ptr(p_draft), _ptr(cand_off), B, M_total, int(capacity),
         int(max_tree), _ptr(rho), _ptr(parent), _ptr(cand_of), _ptr(tree_off), _ptr(workspace),
         _ptr(err), _stream(stream)))
+
+
+def bole_forest_build_noalloc(cand_parent, p_draft, cand_off, capacity, max_tree, rho, parent,
+                              cand_of, tree_off, err=None, stream=None):
+    """bole_forest_build with the library's own fixed device scratch in place of
+    the workspace argument (see bole.h): the same outputs, no allocation."""
+    B, M_total = _forest_args(cand_parent, p_draft, cand_off, capacity, rho, parent, cand_of,
+                              tree_off, err)
+    _check("bole_forest_build_noalloc", lib().bole_forest_build_noalloc(
+        _ptr(cand_parent), _ptr(p_draft), _ptr(cand_off), B, M_total, int(capacity),
+        int(max_tree), _ptr(rho), _ptr(parent), _ptr(cand_of), _ptr(tree_off), _ptr(err),
+        _stream(stream)))

@@ -57,6 +57,7 @@ int bole_conv_commit_launch(int32_t, void*, int32_t, const int32_t*, const void*
 int bole_forest_build_launch(const int32_t*, const float*, const int32_t*, int32_t, int32_t,
                              int32_t, int32_t, float*, int32_t*, int32_t*, int32_t*, void*,
                              uint32_t*, hipStream_t);
+int bole_forest_scratch(size_t, void**);
 int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_t, const void*,
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
@@ -306,6 +307,21 @@ int bole_forest_build(const int32_t* cand_parent, const float* p_draft, const in
   if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return BOLE_E_UNSUPPORTED;
   return bole_forest_build_launch(cand_parent, p_draft, cand_off, B, M_total, capacity, max_tree,
                                   rho, parent, cand_of, tree_off, workspace, err,
+                                  (hipStream_t)stream);
+}
+
+int bole_forest_build_noalloc(const int32_t* cand_parent, const float* p_draft,
+                              const int32_t* cand_off, int32_t B, int32_t M_total,
+                              int32_t capacity, int32_t max_tree, float* rho, int32_t* parent,
+                              int32_t* cand_of, int32_t* tree_off, uint32_t* err, void* stream) {
+  if (!cand_parent || !p_draft || !cand_off || !rho || !parent || !cand_of || !tree_off)
+    return BOLE_E_NULL;
+  if (!forest_shape_ok(B, max_tree) || M_total < 1 || capacity < 1) return BOLE_E_SHAPE;
+  void* scratch = nullptr;
+  const int st = bole_forest_scratch(bole_forest_workspace_bytes(B, max_tree), &scratch);
+  if (st != BOLE_OK) return st;
+  return bole_forest_build_launch(cand_parent, p_draft, cand_off, B, M_total, capacity, max_tree,
+                                  rho, parent, cand_of, tree_off, scratch, err,
                                   (hipStream_t)stream);
 }
 

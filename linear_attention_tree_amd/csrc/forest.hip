@@ -24,6 +24,8 @@
 // packed parent / candidate arrays.  A request's nodes are its
 // selected candidates in key order, so the root is node 0 and parents come
 // first.
+#include <mutex>
+
 #include "common.h"
 
 namespace bole {
@@ -463,6 +465,42 @@ __global__ __launch_bounds__(kPackThreads) void forest_pack_kernel(
 }
 
 }  // namespace bole
+
+// ---------------------------------------------------------------------------
+// Device scratch for bole_forest_build_noalloc: the listed keys and parent
+// positions (12 bytes per listed slot) of the largest shape the builder takes,
+// B * max_tree = kMaxListed, in a fixed array of 192 KiB that each GPU the
+// library runs on holds until the process ends.  Every call on a GPU shares
+// that GPU's copy, so calls that overlap on one GPU race; nothing in it has to
+// start at zero (the scoring kernel writes every listed slot the packing
+// kernel reads).  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+namespace {
+constexpr size_t kForestScratchBytes = 12u * (size_t)bole::kMaxListed;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // the array's device address, per device
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kForestScratchBytes];
+
+// The device address of the scratch array on the current device (resolved on
+// the first call there), for a request of `bytes`.  BOLE_E_SHAPE when it does
+// not fit, BOLE_E_HIP when the runtime cannot name the device or the address.
+extern "C" int bole_forest_scratch(size_t bytes, void** out) {
+  if (bytes > kForestScratchBytes) return BOLE_E_SHAPE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BOLE_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return BOLE_E_HIP;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return BOLE_OK;
+}
 
 extern "C" int bole_forest_build_launch(const int32_t* cand_parent, const float* p_draft,
                                         const int32_t* cand_off, int32_t B, int32_t M_total,

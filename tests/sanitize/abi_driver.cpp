@@ -96,6 +96,13 @@ int bole_commit_launch(int32_t, float*, int64_t, int32_t, const int32_t*, int32_
                        int64_t, const float*, int64_t, const float*, int64_t, const uint64_t*,
                        const int32_t*, const int32_t*, int32_t, int32_t, int32_t, int32_t,
                        int32_t, uint32_t*, hipStream_t) { STUB; }
+// the allocation-free builder's scratch lookup: a fixed host buffer here
+alignas(256) static unsigned char fake_scratch[12 * 16384];
+int bole_forest_scratch(size_t bytes, void** out) {
+  if (bytes > sizeof(fake_scratch)) return BOLE_E_SHAPE;
+  *out = fake_scratch;
+  return BOLE_OK;
+}
 }
 
 int main() {
@@ -210,6 +217,15 @@ int main() {
                                           nullptr));
   REJECTS(BOLE_E_NULL, bole_forest_build(ip, fp, ip, 16, 1872, 1024, 64, fw, iw, iw, iw, nullptr,
                                          err, nullptr));
+
+  // the allocation-free builder: the same checks, no workspace argument
+  LAUNCHES(bole_forest_build_noalloc(ip, fp, ip, 16, 1872, 1024, 64, fw, iw, iw, iw, err, nullptr));
+  LAUNCHES(bole_forest_build_noalloc(ip, fp, ip, 256, 20000, 16384, 64, fw, iw, iw, iw, err,
+                                     nullptr));
+  REJECTS(BOLE_E_SHAPE, bole_forest_build_noalloc(ip, fp, ip, 257, 20000, 16384, 64, fw, iw, iw,
+                                                  iw, err, nullptr));
+  REJECTS(BOLE_E_NULL, bole_forest_build_noalloc(ip, fp, nullptr, 16, 1872, 1024, 64, fw, iw, iw,
+                                                 iw, err, nullptr));
 
   // the multi-layer commit
   LAUNCHES(bole_commit_path(36, fw, 1 << 20, 32, ip, BOLE_BF16, p, 1 << 20, fp, 1 << 20, fp,

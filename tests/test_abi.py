@@ -38,6 +38,7 @@ def test_exports_every_declared_symbol(L):
                           "bole_verify_neumann", "bole_factor_inverse", "bole_verify_inverse",
                           "bole_commit_path", "bole_tree_conv", "bole_conv_commit",
                           "bole_forest_build", "bole_forest_workspace_bytes",
+                          "bole_forest_build_noalloc",
                           "bole_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -49,7 +50,7 @@ def test_internal_launchers_are_hidden(L):
               "bole_verify_neumann_launch", "bole_verify_inverse_launch",
               "bole_factor_inverse_launch", "bole_forest_build_launch",
               "bole_tree_verify_launch", "bole_commit_tree_verify_launch",
-              "bole_tree_conv_launch", "bole_conv_commit_launch"):
+              "bole_tree_conv_launch", "bole_conv_commit_launch", "bole_forest_scratch"):
         with pytest.raises(AttributeError):
             getattr(L, n)
 
