@@ -109,10 +109,25 @@ __device__ __forceinline__ void store_at(float* base, uint32_t off_bytes, const 
   *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off_bytes) = v;
 }
 
-// 16 wait states, kept in place by scheduling barriers.
-__device__ __forceinline__ void swap_gap() {
+// Wait states before a cross-lane read-out, from the CDNA4 (gfx950) table of
+// required independent instructions (the hazards the hardware does not
+// interlock), kept in place by scheduling barriers:
+//  - an XDL (MFMA) VGPR result read by a VALU instruction: passes + 4 on
+//    gfx950; v_mfma_f32_16x16x16_bf16 takes 4 passes, so 8 (s_nop 7);
+//  - a VALU VGPR write read by v_permlane16_swap / v_permlane32_swap (either
+//    operand: both are read and written) or by a DPP instruction: 2 (s_nop 1).
+// The compiler's own hazard pass for gfx950 inserts the same counts (s_nop 7
+// after such an MFMA, s_nop 1 before a swap or a DPP read of a fresh VALU
+// result); the explicit waits hold them at the stage boundaries whatever the
+// scheduler interleaves.
+__device__ __forceinline__ void xdl_read_gap() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7");
+  asm volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void cross_lane_gap() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -268,12 +283,11 @@ struct PathCommit {
     const int c_half = (low ? 0 : 16) + 4 * g4;  // the lane's key within a chunk
 #pragma unroll
     for (int kk = k0; kk < k1; ++kk) {
-      // Explicit wait states before the lines are read out of the update's
-      // accumulators and between the swap stages (each swap writes both of its
-      // registers): with only the compiler's own spacing, the last four lanes
-      // of some rows stored stale values in some runs.
+      // The update's accumulators are MFMA results, read out by the swaps'
+      // operand copies (8 wait states); each swap stage and the rotation read
+      // the previous stage's VALU writes (2 each).
       uint32_t x0[4], x1[4];
-      swap_gap();
+      xdl_read_gap();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, sx[kk][i]),
@@ -282,14 +296,14 @@ struct PathCommit {
         x0[i] = s16[0];
         x1[i] = s16[1];
       }
-      swap_gap();
+      cross_lane_gap();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const auto s32 = __builtin_amdgcn_permlane32_swap(x0[i], x1[i], false, false);
         x0[i] = s32[0];  // line piece g4 (keys 4 g4 .. + 3)
         x1[i] = s32[1];  // line piece 4 + g4
       }
-      swap_gap();
+      cross_lane_gap();
       f32x4 d1, d2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
