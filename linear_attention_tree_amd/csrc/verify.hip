@@ -45,6 +45,7 @@
 //  Inverse  the G and C inputs hold W = (I + G)^-1 and M = C W (formed by
 //           bole_factor_inverse): U = W R and O = B0 + M R, two independent
 //           products with no chain between tiles.
+#include <algorithm>
 #include <type_traits>
 
 #include "tree_topo.h"
@@ -63,7 +64,13 @@ namespace bole {
 // COMMIT (with PREP): the previous round's accepted path of this layer is
 // committed into the slot first (CommitIO), and the verify reads the updated
 // state from registers.
-template <int DT, bool FUSED, bool ONE, bool PREP, int SOLVE = kSolveBlocked, bool COMMIT = false>
+// EARLY (bf16 tokens, blocked solve, V readable as 8-byte pieces): the solve's
+// operands are made visible before phase A and V reaches the accumulator layout
+// through one MFMA against the identity instead of an LDS tile, so each wave
+// goes from its phase A to its solve and readout without waiting for the
+// others.
+template <int DT, bool FUSED, bool ONE, bool PREP, int SOLVE = kSolveBlocked, bool COMMIT = false,
+          bool EARLY = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ logP, const float* __restrict__ beta,
@@ -77,6 +84,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   using SC = StageCfg<DT>;
   static_assert(!(FUSED && SOLVE == kSolveInverse), "W and M come from bole_factor_inverse");
   static_assert(!COMMIT || (FUSED && PREP && SOLVE == kSolveBlocked), "commit inside tree verify");
+  static_assert(!EARLY || (DT == BOLE_BF16 && SOLVE == kSolveBlocked), "early tail: bf16, blocked");
   // O's own products (Q S_pre for B0, C U) carry the split low halves only for
   // float32 tokens; with bf16 tokens O is stored in bf16, and each product is
   // taken at that precision (hi parts: relative error near 2^-8, inside the
@@ -533,6 +541,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     invs[w][0][lane] = wh;
     invs[w][1][lane] = wl;
   }
+  // EARLY: the G/C planes and the diagonal inverses are the only LDS data the
+  // solve and readout read that other waves wrote; they are complete here.
+  // (The barrier waits for LDS traffic only: the state slice stays in flight.)
+  if (EARLY) __syncthreads();
 
   // ---------------- Phase A: [Q;K] S_pre^(r) ----------------
   // V rows of the workgroup's value columns, requested only now (after the
@@ -541,11 +553,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // accumulator layout afterwards.  Rows past the tree read row T-1 and pieces
   // past d_v column 0; both are zeroed.  Without kVecV every piece reads the
   // aligned block holding v[0] and V is fetched element-wise after phase A.
+  // EARLY: the lane's V pieces are the A operands of the identity product,
+  // row 16 mt + l16 of the tile at columns 4 g4 .. + 3 of the wave's 16 (one
+  // 8-byte load per row tile; rows past the tree and pieces past d_v read row
+  // T-1 / column 0 and are zeroed).
   using VC = VTileCfg<DT>;
   using VElem = std::conditional_t<DT == BOLE_BF16, uint16_t, uint32_t>;
   const bool vvec = vecf & kVecV;
   u16x8 vpc[VC::PER];
-  {
+  bf16x4 va[4];
+  if (EARLY) {
+    const int c4 = kBV * r + 16 * w + 4 * g4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = 16 * mt + l16;
+      const bool in = row < T && c4 < d_v;
+      const int64_t e =
+          ((int64_t)(off + rowNode[min(row, T - 1)]) * H + h) * d_v + (c4 < d_v ? c4 : 0);
+      const u16x4 raw = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(v) + e);
+      va[mt] = __builtin_bit_cast(bf16x4, in ? raw : u16x4{0, 0, 0, 0});
+    }
+  } else {
     const u16x8* vsafe = reinterpret_cast<const u16x8*>(reinterpret_cast<uintptr_t>(v) & ~uintptr_t(15));
 #pragma unroll
     for (int it = 0; it < VC::PER; ++it) {
@@ -629,17 +657,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       }
     }
   }
-  __syncthreads();  // diagonal inverses visible; staged Q/K rows no longer read
-  // Past this point the workgroup holds all its inputs and only its tail is
-  // left: its waves take issue priority over waves still in their load phases
-  // (the two workgroups of a CU otherwise finish about 3 us apart at the
-  // target shape; measured 0.6 us faster).  Wave priority only orders issue
-  // among resident waves.
+  if (!EARLY) __syncthreads();  // diagonal inverses visible; staged Q/K rows no longer read
+  // Past this point the wave holds all its inputs and only its tail is left:
+  // it takes issue priority over waves still in their load phases (the two
+  // workgroups of a CU otherwise finish about 3 us apart at the target shape;
+  // measured 0.6 us faster).  Wave priority only orders issue among resident
+  // waves.
   __builtin_amdgcn_s_setprio(2);
 
-  // V tile into LDS (over the staged rows)
+  // V tile into LDS (over the staged rows); EARLY: V in the accumulator layout
+  // by D = V_tile x I on v_mfma_f32_16x16x16_bf16 (exact: one bf16 product
+  // with 1.0 per entry), the lane's rows 16 mt + 4 g4 + e of column vloc
   VElem* vt = reinterpret_cast<VElem*>(stage);
-  if (vvec) {
+  f32x4 vacc[4];
+  if (EARLY) {
+    bf16x4 ident;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ident[e] = (__bf16)(4 * g4 + e == l16 ? 1.0f : 0.0f);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vacc[mt] = mfma16_bf16(va[mt], ident, zero_f32x4());
+  } else if (vvec) {
 #pragma unroll
     for (int it = 0; it < VC::PER; ++it) {
       const int id = threadIdx.x + kThreads * it;
@@ -656,7 +693,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       vt[vtile_idx(row, c)] = x;
     }
   }
-  __syncthreads();  // V tile visible
+  if (!EARLY) __syncthreads();  // V tile visible
 
   // B0 = D_P QS, R = D_beta (V - D_P KS); rows beyond the tree are exact zeros.
   f32x4 ru[4];
@@ -666,8 +703,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int e = 0; e < 4; ++e) {
       const int p = 16 * mt + 4 * g4 + e;
       const float P = rowP[p], bt = rowBeta[p];
-      const VElem raw = vt[vtile_idx(p, vloc)];
-      const float vx = __builtin_bit_cast(float, DT == BOLE_BF16 ? (uint32_t)raw << 16 : (uint32_t)raw);
+      float vx;
+      if (EARLY) {
+        vx = vacc[mt][e];
+      } else {
+        const VElem raw = vt[vtile_idx(p, vloc)];
+        vx = __builtin_bit_cast(float, DT == BOLE_BF16 ? (uint32_t)raw << 16 : (uint32_t)raw);
+      }
       qs[mt][e] = P * qs[mt][e];
       ru[mt][e] = bt * (vx - P * ks[mt][e]);
     }
@@ -825,7 +867,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // The tiles are written to LDS in the accumulator layout and leave as 4-element
   // pieces of the nodes' rows (16 bytes of U, 8 or 16 of O per lane).
   using OElem = std::conditional_t<DT == BOLE_BF16, uint16_t, float>;
-  __syncthreads();  // every wave is done with the V tile and the C planes
+  __syncthreads();  // every wave is done with the staged rows, the V tile and the C planes
   float* ut = reinterpret_cast<float*>(stage);
   OElem* ot = reinterpret_cast<OElem*>(gcs);
 #pragma unroll
@@ -886,15 +928,59 @@ int launch_verify_t(const void* q, const void* k, const void* v, const float* lo
                     int32_t d_v, void* O, float* U, uint32_t* err, hipStream_t s,
                     bole::PrepIO prep = bole::PrepIO{}, bole::CommitIO cm = bole::CommitIO{}) {
   const int NV = (d_v + bole::kBV - 1) / bole::kBV;
-  const dim3 grid(B * H * NV), block(bole::kThreads);
+  const dim3 block(bole::kThreads);
   const int esize = DT == BOLE_BF16 ? 2 : 4;
   const bool v_ok = d_v % (16 / esize) == 0 && (uintptr_t)v % 16 == 0;
   const bool out_ok = d_v % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)O % (4 * esize) == 0;
   const int vecf = (v_ok ? bole::kVecV : 0) | (out_ok ? bole::kVecOut : 0);
-  hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT>), grid, block, 0, s, q,
-                     k, v, logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth, tree_off,
-                     tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err, cm);
-  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
+  // the early tail (fused producer only: without Gram work, half the waves
+  // would wait at its barrier) reads V as 8-byte pieces of four columns
+  constexpr bool kMayEarly = DT == BOLE_BF16 && SOLVE == bole::kSolveBlocked && FUSED;
+  const bool early = kMayEarly && d_v % 4 == 0 && (uintptr_t)v % 8 == 0;
+  // A grid larger than one round of resident workgroups (two per CU) runs as
+  // request chunks of at most one round each, back to back on the stream: the
+  // workgroups of a chunk start together and move through their phases in
+  // step, where a second residency round inside one launch starts piecemeal
+  // as first-round workgroups finish.  Each chunk sees the per-request arrays
+  // from its first request on.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 1 << 20;  // unknown: one launch
+  const int64_t per_req = (int64_t)H * NV;
+  const int64_t cap = 2 * (int64_t)cus;
+  const int max_req = (int)std::max<int64_t>(1, cap / per_req);
+  const int chunks = (B + max_req - 1) / max_req;
+  const int per_chunk = (B + chunks - 1) / chunks;
+  for (int b0 = 0; b0 < B; b0 += per_chunk) {
+    const int Bc = std::min(per_chunk, B - b0);
+    const int64_t gc = (int64_t)b0 * H * bole::kMaxTree * bole::kMaxTree;
+    bole::PrepIO pr = prep;
+    if (pr.tree_depth) pr.tree_depth += b0;
+    bole::CommitIO cc = cm;
+    if (cc.accept) cc.accept += b0;
+    if (cc.tree_off) cc.tree_off += b0;
+    const dim3 grid(Bc * H * NV);
+    const int32_t* slot_c = slot + b0;
+    const int32_t* off_c = tree_off + b0;
+    const int32_t* td_c = tree_depth ? tree_depth + b0 : nullptr;
+    const float* G_c = G ? G + gc : nullptr;
+    const float* C_c = C ? C + gc : nullptr;
+    if (early) {
+      if constexpr (kMayEarly)
+        hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT, true>), grid,
+                           block, 0, s, q, k, v, logP, beta, state_pool, n_slots, slot_c, G_c,
+                           C_c, anc, order, depth, off_c, td_c, Bc, N, H, d_k, d_v, O, U, vecf, pr,
+                           err, cc);
+    } else {
+      hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT>), grid, block, 0,
+                         s, q, k, v, logP, beta, state_pool, n_slots, slot_c, G_c, C_c, anc, order,
+                         depth, off_c, td_c, Bc, N, H, d_k, d_v, O, U, vecf, pr, err, cc);
+    }
+    if (hipGetLastError() != hipSuccess) return BOLE_E_HIP;
+  }
+  return BOLE_OK;
 }
 
 template <bool FUSED, int SOLVE = bole::kSolveBlocked>
