@@ -1,8 +1,9 @@
 """Build libbole.so (HIP, gfx950) in-tree.
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked
-into linear_attention_tree_amd/libbole.so.  hipcc cross-compiles for gfx950
-without a GPU present.
+into linear_attention_tree_amd/libbole.so; the measurement baselines under
+baselines/ go into baselines/libbole_baselines.so.  hipcc cross-compiles for
+gfx950 without a GPU present.
 """
 
 from __future__ import annotations
@@ -20,6 +21,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libbole.so")
+# measurement baselines (not part of libbole's interface)
+BASELINE_DIR = os.path.join(HERE, "baselines")
+BASELINE_LIB_PATH = os.path.join(BASELINE_DIR, "libbole_baselines.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -43,10 +47,18 @@ def sources():
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Build libbole.so and the measurement baselines' library; returns the
+    path of libbole.so."""
+    path = _build_lib(sources(), LIB_PATH, "", verbose, jobs)
+    _build_lib(sorted(glob.glob(os.path.join(BASELINE_DIR, "*.hip"))), BASELINE_LIB_PATH,
+               "baseline_", verbose, jobs)
+    return path
+
+
+def _build_lib(srcs, lib_path, prefix, verbose, jobs):
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(BUILD_DIR, prefix + os.path.basename(s)[:-4] + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
@@ -61,13 +73,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -368,6 +368,15 @@ def device_layer(cfg: Config, N: int, layer: int, seed: int, torch, dev, lead=()
                        beta=beta.contiguous())
 
 
+def device_states(cfg: Config, n_slots: int, seed: int, torch, dev, lead=()):
+    """Committed states drawn directly on the device, [*lead, n_slots, H, d_v,
+    d_k] float32 with N(0, STATE_STD^2) entries (the spread of prefix-built
+    states; see make_states)."""
+    gen = _device_gen(torch, dev, cfg, STREAM_PREFIX, seed, 1 << 22)
+    return torch.randn(*lead, n_slots, cfg.H, cfg.d_v, cfg.d_k, generator=gen, device=dev,
+                       dtype=torch.float32) * STATE_STD
+
+
 def device_prefix(cfg: Config, B: int, layer: int, seed: int, torch, dev) -> DeviceLayer:
     """The committed-prefix tokens of all B x H state heads of one layer,
     [P, B, H, ...] (P = cfg.prefix)."""
