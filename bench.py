@@ -38,9 +38,9 @@ KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_tree_amd", "csrc", f)
                   for f in KERNEL_SOURCE_NAMES]
 # the bf16 verify kernel with preparation and the previous round's commit
 # inside, which the default step launches (name as rocprofv3 prints it)
-DOMINANT_KERNEL = "verify_kernel<1, true, true, true, 0, true>"
+DOMINANT_KERNEL = "verify_kernel<1, true, true, true, 0, true, true>"
 # the same without the commit (bole_tree_verify)
-TREE_VERIFY_KERNEL = "verify_kernel<1, true, true, true, 0, false>"
+TREE_VERIFY_KERNEL = "verify_kernel<1, true, true, true, 0, false, true>"
 
 
 def verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
@@ -145,8 +145,8 @@ def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
     forests = [W.make_forest(cfg, seed) for seed in range(4)]
     algo = {
         "bole::" + DOMINANT_KERNEL: np.mean(
-            [commit_tree_verify_algorithmic_bytes(f.sizes(), forests[i - 1], cfg.H, cfg.d_k,
-                                                  cfg.d_v, 2) for i, f in enumerate(forests)]),
+            [commit_tree_verify_algorithmic_bytes(f.sizes(), f, cfg.H, cfg.d_k, cfg.d_v, 2)
+             for f in forests]),
         "bole::" + TREE_VERIFY_KERNEL: np.mean(
             [tree_verify_algorithmic_bytes(f.sizes(), cfg.H, cfg.d_k, cfg.d_v, 2) for f in forests]),
         "bole::commit_kernel<1>": np.mean(
@@ -203,6 +203,20 @@ def summarize_mfma(mfma_dir, trace_dir, command):
     print("\n".join(lines))
 
 
+def timed_window(trace_dir, kernel):
+    """Durations (ns) of `kernel`'s dispatches in the timed region of a kernel
+    trace: the first stretch between two consecutive spin-kernel dispatches
+    that holds that kernel's dispatches and nothing else (the bench puts a
+    spin before and after its timed replays).  None when there is none."""
+    rows = sorted(_csv_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    spins = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
+    for a, b in zip(spins, spins[1:]):
+        win = rows[a + 1:b]
+        if win and all(kernel in r["Kernel_Name"] for r in win):
+            return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in win]
+    return None
+
+
 def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     """Turn three rocprofv3 runs of this script (a kernel trace, a FETCH_SIZE
     pass and a WRITE_SIZE pass, the counter passes preceded by a plain copy of
@@ -210,9 +224,27 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     record the bench line reads its `traffic` from."""
     os.makedirs(PROFILES, exist_ok=True)
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    cfg = W.CONFIGS["target"]
+    forests = [W.make_forest(cfg, seed) for seed in range(4)]
+    # the default step's launches each commit their own batch's previous round
+    algo = float(np.mean([commit_tree_verify_algorithmic_bytes(f.sizes(), f, cfg.H, cfg.d_k,
+                                                               cfg.d_v, 2) for f in forests]))
     lines = ["# Kernel durations, target workload (rocprofv3 --kernel-trace --stats)", "",
-             "Command:", "", "```", commands["trace"], "```", "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+             "Command:", "", "```", commands["trace"], "```", ""]
+    win = timed_window(trace_dir, DOMINANT_KERNEL)
+    if win:
+        w = np.array(win, np.float64) / 1e3
+        lines += ["## The timed region", "",
+                  "Dispatches of `bole_commit_tree_verify` between the two spin-kernel markers "
+                  "the bench launches around its timed replays (the K steps its JSON line "
+                  "reports):", "",
+                  "| dispatches | mean us | median us | min us | max us | algorithmic MB | "
+                  "GB/s at the mean | of 8 TB/s |", "|---|---|---|---|---|---|---|---|",
+                  f"| {len(w)} | {w.mean():.2f} | {np.median(w):.2f} | {w.min():.2f} | "
+                  f"{w.max():.2f} | {algo / 1e6:.1f} | {algo / (w.mean() * 1e3):.0f} | "
+                  f"{algo / (w.mean() * 1e3) / PEAK_HBM_GBS:.3f} |", ""]
+    lines += ["## Every dispatch of the run (warm-up, captures and other paths included)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         if "bole::" in r["Name"] or "copyBuffer" in r["Name"]:
             lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
@@ -234,10 +266,6 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
     calib_kib = calib_mib * 1024.0
     f_fetch, f_write = calib_kib / copy_fetch, calib_kib / copy_write
     traffic = (fetch * f_fetch + write * f_write) * 1024.0
-    cfg = W.CONFIGS["target"]
-    forests = [W.make_forest(cfg, seed) for seed in range(4)]
-    algo = np.mean([commit_tree_verify_algorithmic_bytes(f.sizes(), forests[i - 1], cfg.H, cfg.d_k,
-                                                         cfg.d_v, 2) for i, f in enumerate(forests)])
     rec = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": kernel_source_hash(),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [n_f, n_w], "copy_mib": calib_mib,
@@ -301,6 +329,14 @@ def build_states_on_gpu(cfg, B, layer, seed, torch, TreeRound, dev):
 
 
 class InputSet:
+    """One request batch's round inputs on the device: its forest, token
+    operands and slot states.  The deferred step (each launch commits the same
+    requests' previous round) reads the previous round's U, logP and topology
+    while writing its own, so those outputs rotate through GROUPS buffer groups
+    (group 0 is also what the other paths use)."""
+
+    GROUPS = 3
+
     def __init__(self, cfg, seed, torch, TreeRound, dev):
         f = W.make_forest(cfg, seed)
         x = W.make_layer(cfg, f.N, 0, seed)
@@ -324,9 +360,51 @@ class InputSet:
         self.logP = torch.empty_like(self.g)
         self.O = torch.empty(N, H, cfg.d_v, dtype=self.v.dtype, device=dev)
         self.U = torch.empty(N, H, cfg.d_v, dtype=torch.float32, device=dev)
+        t = self.rnd.topo
+        self.groups = [dict(U=self.U, logP=self.logP[0], depth=t.depth, anc=t.anc,
+                            order=t.order, tree_depth=t.tree_depth)]
+        for _ in range(self.GROUPS - 1):
+            self.groups.append(dict(
+                U=torch.empty_like(self.U), logP=torch.empty_like(self.logP[0]),
+                depth=torch.empty_like(t.depth), anc=torch.empty_like(t.anc),
+                order=torch.empty_like(t.order), tree_depth=torch.empty_like(t.tree_depth)))
+
+    def fill_groups(self, bole):
+        """Every group holds a verified round of this batch (bole_tree_verify
+        from the current slot states, which it leaves unchanged)."""
+        t = self.rnd.topo
+        for gr in self.groups:
+            bole.bole_tree_verify(self.q, self.k, self.v, t.parent, self.g[0], self.beta,
+                                  self.pool, self.slot, t.tree_off, self.O, gr["U"], gr["depth"],
+                                  gr["anc"], gr["order"], gr["tree_depth"], gr["logP"],
+                                  self.rnd.err)
 
 
-def launch(s, bole, which):
+def cycle_colour(m, n):
+    """Output group of a batch's m-th round when its n >= 2 rounds repeat as a
+    cycle (graph replays): a proper colouring of the cycle, so a round never
+    writes the group its predecessor (round m - 1, or n - 1 for m = 0) wrote."""
+    if n % 2 == 0 or m < n - 1:
+        return m % 2
+    return 2
+
+
+def deferred_schedule(R, S):
+    """(set, written group, read group) of each of R deferred steps over S sets
+    in rotation: step i runs set i % S, whose rounds in the R steps form a cycle
+    (each needs at least two)."""
+    if R < 2 * S:
+        raise SystemExit(f"the deferred step needs at least {2 * S} steps per graph "
+                         f"(two rounds per input set); got {R}")
+    out = []
+    for i in range(R):
+        j, m = i % S, i // S
+        n = (R - j + S - 1) // S
+        out.append((j, cycle_colour(m, n), cycle_colour((m - 1) % n, n)))
+    return out
+
+
+def launch(s, bole, which, cur=0, prev=1):
     t = s.rnd.topo
     lp = s.logP[0]
     if which == "tree_prep":
@@ -357,13 +435,13 @@ def launch(s, bole, which):
         bole.bole_commit_path(s.pool, s.slot, s.k, s.U, lp, t.anc, t.tree_off, s.accept,
                               s.rnd.err)
     elif which == "commit_tree_verify":
-        # the previous input set's round is committed into this set's slots:
-        # the same work as a serving loop's previous round of the same requests
-        p, pt = s.prev, s.prev.rnd.topo
+        # the same requests' previous round (group `prev`) is committed into
+        # their slots, and this round is verified and written to group `cur`
+        gc, gp = s.groups[cur], s.groups[prev]
         bole.bole_commit_tree_verify(s.q, s.k, s.v, t.parent, s.g[0], s.beta, s.pool, s.slot,
-                                     t.tree_off, s.O, s.U, t.depth, t.anc, t.order, t.tree_depth,
-                                     lp, p.k, p.U, p.logP[0], pt.anc, pt.tree_off, p.accept,
-                                     s.rnd.err)
+                                     t.tree_off, s.O, gc["U"], gc["depth"], gc["anc"],
+                                     gc["order"], gc["tree_depth"], gc["logP"], s.k, gp["U"],
+                                     gp["logP"], gp["anc"], t.tree_off, s.accept, s.rnd.err)
     else:
         raise ValueError(which)
 
@@ -385,10 +463,11 @@ STEPS = {
 }
 
 
-def run_step(s, bole, path="tree"):
-    """One pass of the whole path on the current stream."""
+def run_step(s, bole, path="tree", cur=0, prev=1):
+    """One pass of the whole path on the current stream (cur / prev: the
+    deferred step's written and read output groups)."""
     for which in STEPS[path]:
-        launch(s, bole, which)
+        launch(s, bole, which, cur, prev)
 
 
 def capture(torch, fn):
@@ -408,16 +487,34 @@ def capture(torch, fn):
 
 def time_graphs(graphs, reps, torch):
     """Average ms per replay of graphs[i % len(graphs)], i < reps, bracketed by
-    events on the replaying (current) stream."""
+    events on the replaying (current) stream.  An untimed replay of each graph
+    goes first, not waited for, so the GPU is busy when the timed region
+    opens."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
     e0.record()
     for i in range(reps):
         graphs[i % len(graphs)].replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def graph_steps(k, cap=2048):
+    """Steps per captured graph for a run of exactly k steps: k itself, or the
+    largest divisor of k not above cap."""
+    if k <= cap:
+        return k
+    return next(r for r in range(cap, 0, -1) if k % r == 0)
+
+
+# Spin kernel ahead of each timed region (torch.cuda._sleep cycles, about a
+# millisecond): long enough for the host to enqueue the timed replays before the
+# GPU reaches them.
+SPIN_COVER_CYCLES = 2_000_000
 
 
 def time_steps_eager(sets, bole, path, K, torch):
@@ -456,6 +553,19 @@ def check_graph_replay(s, graph, bole, path, torch):
     torch.cuda.synchronize()
 
 
+def cpu_model():
+    """The host CPU's model name as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, seed, budget_s=12.0):
     """The fp64 oracle (tree walk + commit) on the host cores, on the same
     workload; repeats the whole layer until about budget_s of CPU work."""
@@ -483,6 +593,7 @@ def cpu_baseline(cfg, seed, budget_s=12.0):
     reps1, el1 = timed(1, budget_s / 4)
     rate = reps * f.N * cfg.H / el
     return {"value": rate, "unit": "node-heads/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{reps} full repetitions of the workload's layer (prep + walk + commit, "
                       f"{f.N} nodes x {cfg.H} heads, float64) in {el:.1f} s",
             "single_thread_value": reps1 * f.N * cfg.H / el1}
@@ -671,6 +782,169 @@ def time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K):
             "deferred_by_capacity": out_d}
 
 
+def multilayer_record(torch, TreeRound, bole, dev, reps):
+    """The multi-layer round at its full shape (36 layers, 32 trees x 64 nodes,
+    32 heads, d = 128, bf16; token operands and states drawn on the device)
+    beside the per-node full-state-snapshot baseline run in the same harness:
+    round times, the per-layer kernels against their roofline, the commit over
+    all layers, bytes written per layer and the snapshots' resident memory."""
+    from linear_attention_tree_amd.baselines import SnapshotVerifier
+    cfg = W.CONFIGS["multilayer"]
+    L, H, d_k, d_v = cfg.L, cfg.H, cfg.d_k, cfg.d_v
+    f = W.make_forest(cfg, 0)
+    B, N = f.B, f.N
+    e = 2 if cfg.dtype == "bf16" else 4
+    x = W.device_layer(cfg, N, 0, 0, torch, dev, lead=(L,))
+    pool0 = W.device_states(cfg, B, 0, torch, dev, lead=(L,))
+    slot = torch.arange(B, dtype=torch.int32, device=dev)
+    accept = torch.from_numpy(f.accept).to(dev)
+    rnd = TreeRound(f.parent, f.tree_off, H, device=dev)
+    t = rnd.topo
+    O = torch.empty(L, N, H, d_v, dtype=x.v.dtype, device=dev)
+    # two output sets: a deferred round reads the previous round's U, logP and
+    # ancestor sets while it writes its own
+    bufs = [(torch.empty(L, N, H, d_v, dtype=torch.float32, device=dev),
+             torch.empty(L, N, H, dtype=torch.float32, device=dev),
+             tuple(torch.empty_like(a) for a in (t.depth, t.anc, t.order, t.tree_depth)))
+            for _ in range(2)]
+    pool = pool0.clone()
+
+    def tree_layer(l, U, lp, topo):
+        bole.bole_tree_verify(x.q[l], x.k[l], x.v[l], t.parent, x.g[l], x.beta[l], pool[l], slot,
+                              t.tree_off, O[l], U[l], *topo, lp[l], rnd.err)
+
+    def deferred_layer(l, cur):
+        (U, lp, topo), (Up, lpp, topop) = bufs[cur], bufs[1 - cur]
+        bole.bole_commit_tree_verify(x.q[l], x.k[l], x.v[l], t.parent, x.g[l], x.beta[l],
+                                     pool[l], slot, t.tree_off, O[l], U[l], *topo, lp[l],
+                                     x.k[l], Up[l], lpp[l], topop[1], t.tree_off, accept, rnd.err)
+
+    def tree_round(cur=0):  # L x bole_tree_verify, then one commit over all layers
+        U, lp, topo = bufs[cur]
+        for l in range(L):
+            tree_layer(l, U, lp, topo)
+        bole.bole_commit_path(pool, slot, x.k, U, lp, topo[1], t.tree_off, accept, rnd.err)
+
+    def deferred_rounds():  # two rounds of L x bole_commit_tree_verify
+        for cur in (0, 1):
+            for l in range(L):
+                deferred_layer(l, cur)
+
+    def commit_only():
+        U, lp, topo = bufs[0]
+        bole.bole_commit_path(pool, slot, x.k, U, lp, topo[1], t.tree_off, accept, rnd.err)
+
+    def timed(fn, n_rep):
+        """ms per replay of fn's captured graph: pre-roll replays, then a busy
+        spin while the host enqueues the timed replays."""
+        g = capture(torch, fn)
+        for _ in range(2):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_COVER_CYCLES)
+        e0.record()
+        for _ in range(n_rep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_rep
+
+    tree_round(0)  # real rounds in both buffer sets
+    tree_round(1)
+    torch.cuda.synchronize()
+    ms_deferred = timed(deferred_rounds, max(reps // 8, 3)) / 2
+    ms_tree = timed(tree_round, max(reps // 8, 3))
+    ms_commit = timed(commit_only, max(reps // 4, 5))
+    # per launch: marginal time between one and two deferred rounds' launches,
+    # and between L and 2L tree_verify launches
+    t1 = timed(lambda: [deferred_layer(l, 0) for l in range(L)], 3)
+    t2 = timed(deferred_rounds, 3)
+    ms_ctv = (t2 - t1) / L
+    U0, lp0, topo0 = bufs[0]
+    t1 = timed(lambda: [tree_layer(l, U0, lp0, topo0) for l in range(L)], 3)
+    t2 = timed(lambda: [tree_layer(l % L, U0, lp0, topo0) for l in range(2 * L)], 3)
+    ms_tv = (t2 - t1) / L
+    assert rnd.error_bits() == 0, "device error bits set"
+    ctv_bytes = commit_tree_verify_algorithmic_bytes(f.sizes(), f, H, d_k, d_v, e)
+    tv_bytes = tree_verify_algorithmic_bytes(f.sizes(), H, d_k, d_v, e)
+    c_bytes = commit_algorithmic_bytes(f, L, H, d_k, d_v, e)
+
+    # the per-node snapshot baseline on the same inputs: every layer's node
+    # states kept until the round's commit, as a serial tree verifier keeps them
+    snap_layer = N * H * d_v * d_k * 4
+    free, _ = torch.cuda.mem_get_info()
+    all_layers = free > L * snap_layer + (8 << 30)
+    snap = torch.empty((L if all_layers else 1), N, H, d_v, d_k, dtype=torch.float32, device=dev)
+    sv = SnapshotVerifier(f.parent, f.tree_off, H, device=dev)
+    pool_s = pool0.clone()
+    O_s = torch.empty_like(O)
+    U_s = torch.empty_like(bufs[0][0])
+
+    def snapshot_layer(l):
+        sl = snap[l if all_layers else 0]
+        sv.layer(x.q[l], x.k[l], x.v[l], x.g[l], x.beta[l], pool_s[l], slot, sl, O_s[l], U_s[l])
+        if not all_layers:  # commit before the next layer overwrites the snapshots
+            sv.commit(sl, pool_s[l], slot, accept)
+
+    def snapshot_round():
+        for l in range(L):
+            snapshot_layer(l)
+        if all_layers:
+            for l in range(L):
+                sv.commit(snap[l], pool_s[l], slot, accept)
+
+    snapshot_round()
+    torch.cuda.synchronize()
+    ms_snap = timed(snapshot_round, 3)
+    ms_snap_layer = timed(lambda: snapshot_layer(0), 5)
+    del snap
+    torch.cuda.empty_cache()
+    o_u_bytes = N * H * d_v * (e + 4)
+    prep_bytes = N * (4 * H + 20)
+    snap_written = snap_layer + o_u_bytes
+    snap_moved = 2 * snap_layer + N * H * (2 * e * d_k + e * d_v + 8) + o_u_bytes
+    return {
+        "workload": f"L={L} layers, B={B} trees x T={cfg.T} nodes (random recursive, "
+                    f"depth<={cfg.D}), H={H}, d_k=d_v={d_k}, {cfg.dtype} q/k/v, f32 gates and "
+                    "state; tokens and states drawn on the device",
+        "round_ms": {"deferred: L x commit_tree_verify": ms_deferred,
+                     "tree: L x tree_verify + one commit over all layers": ms_tree},
+        "node_heads_per_s_per_layer": N * H * L / (ms_deferred * 1e-3),
+        "commit_tree_verify_per_layer": {
+            "ms": ms_ctv, "algorithmic_bytes": ctv_bytes,
+            "frac_of_hbm_peak": ctv_bytes / (ms_ctv * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "tree_verify_per_layer": {
+            "ms": ms_tv, "algorithmic_bytes": tv_bytes,
+            "frac_of_hbm_peak": tv_bytes / (ms_tv * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "commit_over_all_layers": {
+            "ms": ms_commit, "algorithmic_bytes": c_bytes,
+            "frac_of_hbm_peak": c_bytes / (ms_commit * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "gc_bytes_per_round": {"tree and deferred paths (on chip)": 0,
+                               "split path: one workspace reused by every layer":
+                               int(bole.bole_gc_workspace_bytes(B, H))},
+        "bytes_written_per_layer": {
+            "bole_tree_verify (O, U, logP, topology)": o_u_bytes + prep_bytes,
+            "bole_commit_tree_verify (also the committed slots)":
+                o_u_bytes + prep_bytes + B * H * d_v * d_k * 4,
+            "snapshot baseline (node states, O, U)": snap_written},
+        "snapshot_baseline": {
+            "note": "per-node full-state snapshots, level-synchronous (one launch per depth; "
+                    "every node's float32 state written, then read by its children); commit = "
+                    "copy of the accepted node's state",
+            "ms_per_round": ms_snap, "ms_per_layer": ms_snap_layer,
+            "bytes_moved_per_layer": snap_moved,
+            "GBs_per_layer": snap_moved / (ms_snap_layer * 1e-3) / 1e9,
+            "resident_snapshot_GiB": (L if all_layers else 1) * snap_layer / 2 ** 30,
+            "snapshots_kept": "every layer until the commit" if all_layers
+                              else "one layer at a time (not enough free memory for all)",
+        },
+        "round_speedup_vs_snapshot": ms_snap / ms_deferred,
+        "transient_bytes_per_round": {"U + logP": L * N * H * (4 * d_v + 4),
+                                      "per-node snapshots": L * snap_layer},
+    }
+
+
 def round_main(cfg, args, torch, TreeRound, bole, dev):
     """One step = one verification round over cfg.L layers: the per-layer
     verify launches, then one commit over all layers (in place, so each round
@@ -845,6 +1119,8 @@ def main():
                          "split: the four calls; split_neumann, split_inverse: the four calls "
                          "with the other exact solves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-multilayer", action="store_true",
+                    help="leave out the 36-layer round and its per-node snapshot baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -888,54 +1164,88 @@ def main():
     if args.sets < 2:
         raise SystemExit("--sets must be at least 2 (a step commits the previous set's round)")
     sets = [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(args.sets)]
-    for i, s_ in enumerate(sets):
-        s_.prev = sets[i - 1]  # the round before this one, in the rotation
+    S = len(sets)
     e = 2 if cfg.dtype == "bf16" else 4
+    for s_ in sets:
+        s_.fill_groups(bole)
 
     for i in range(args.warmup):
         for p in STEPS:
-            run_step(sets[i % len(sets)], bole, p)
+            run_step(sets[i % S], bole, p)
     torch.cuda.synchronize()
     for s in sets:
         assert s.rnd.error_bits() == 0, "device error bits set"
 
-    # The step is timed as HIP graph replays (one captured step per input set,
-    # replayed in rotation): launching three kernels per step from Python costs
-    # more host time than the GPU spends on them.
+    # Steps are timed as replays of one captured graph of R steps (R = K, or a
+    # divisor of K for long runs): launching a kernel per step from Python
+    # costs more host time than the GPU spends on it.  Batches rotate over the
+    # input sets; with the deferred step each set's rounds form a cycle in
+    # which every launch commits the same requests' previous round.
     K = args.steps
-    others = [p for p in STEPS if p != args.path]
-    R = 4 * len(sets)  # steps per rotation graph
-    singles = [capture(torch, lambda s_=s_: run_step(s_, bole, args.path)) for s_ in sets]
-    check_graph_replay(sets[0], singles[0], bole, args.path, torch)
+    check_graph_replay(sets[0], capture(torch, lambda: run_step(sets[0], bole, args.path)),
+                       bole, args.path, torch)
 
-    def rotation(p):
-        return capture(torch, lambda: [run_step(sets[i % len(sets)], bole, p) for i in range(R)])
+    def launches(which, r):
+        """r launches of one kernel (or one step when `which` is a path) over
+        the rotated sets, as a list of zero-argument calls."""
+        if which in ("deferred", "commit_tree_verify"):
+            name = "commit_tree_verify"
+            return [lambda j=j, c=c, pv=pv: launch(sets[j], bole, name, c, pv)
+                    for j, c, pv in deferred_schedule(r, S)]
+        if which in STEPS:
+            return [lambda i=i: run_step(sets[i % S], bole, which) for i in range(r)]
+        return [lambda i=i: launch(sets[i % S], bole, which) for i in range(r)]
 
-    def time_k_steps(p, k, singles_p):
-        """Exactly k steps: k // R rotation replays, then the rest one by one,
-        after an untimed pre-roll of the same graph (the GPU otherwise enters
-        the timed region idle, right after the host-side captures)."""
-        rot = rotation(p)
-        for _ in range(max(1, min(k, 200) // R)):
-            rot.replay()
+    def time_graph(g, r, replays, marker=False):
+        """ms per step of `replays` back-to-back replays of the captured graph
+        g of r steps, after untimed pre-roll replays.  A long spin kernel ahead
+        of the first timed replay keeps the GPU busy while the host enqueues
+        the timed replays, so the timed region holds no host launch time; it
+        only holds the GPU's own start of each replay.  marker: the spin and a
+        short one after the timed replays delimit them in a kernel trace."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        for _ in range(max(1, -(-200 // r))):
+            g.replay()
+        torch.cuda._sleep(SPIN_COVER_CYCLES)
         e0.record()
-        for _ in range(k // R):
-            rot.replay()
-        for i in range(k % R):
-            singles_p[i % len(sets)].replay()
+        for _ in range(replays):
+            g.replay()
         e1.record()
+        if marker:
+            torch.cuda._sleep(1000)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / k
+        return e0.elapsed_time(e1) / (replays * r)
 
-    ms_step = time_k_steps(args.path, K, singles)
-    ms_other = {}
-    for other in others:
-        singles_other = [capture(torch, lambda s_=s_, o_=other: run_step(s_, bole, o_))
-                         for s_ in sets]
-        ms_other[other] = time_k_steps(other, max(K // 2, 10), singles_other)
+    def capture_steps(which, r):
+        calls = launches(which, r)
+        return capture(torch, lambda: [c() for c in calls])
+
+    def time_k(which, k, marker=False):
+        """ms per step over exactly k back-to-back steps (k / r replays of one
+        graph of r steps)."""
+        r = graph_steps(k)
+        return time_graph(capture_steps(which, r), r, k // r, marker)
+
+    def time_per_launch(which, r=64, replays=8):
+        """Marginal ms per launch of back-to-back launches: the difference
+        between graphs of 2r and r launches, each replayed `replays` times
+        after the busy spin.  The GPU's start of each replay cancels, so this
+        is the kernel's own duration in a stream of launches, the figure a
+        kernel trace reports per dispatch."""
+        t1 = time_graph(capture_steps(which, r), r, replays) * r
+        t2 = time_graph(capture_steps(which, 2 * r), 2 * r, replays) * 2 * r
+        return (t2 - t1) / r
+
+    torch.cuda._sleep(1)  # load the spin kernel before the timed regions
+    ms_step = time_k(args.path, K, marker=True)
+    # the dominant kernel's own duration per launch (the step's one launch
+    # for the deferred path), and the verify kernel alone (the step's verify
+    # without the commit), each as the marginal time per back-to-back launch
+    ms_launch = time_per_launch(args.path if args.path == "deferred" else DOMINANT[args.path][0])
+    ms_tree_verify = time_per_launch("tree_verify")
+    ms_other = {p: time_k(p, max(K // 2, 2 * S)) for p in STEPS if p != args.path}
     ms_eager = time_steps_eager(sets, bole, args.path, max(K // 2, 10), torch)
     # per-kernel averages: each kernel alone, 4 x len(sets) launches per graph
     # over the rotated sets (same inputs, same stream)
@@ -943,9 +1253,9 @@ def main():
                "commit_tree_verify", "verify_neumann", "factor_inverse", "verify_inverse")
     avg = {}
     for which in kernels:
-        n_in = 4 * len(sets)
-        g = capture(torch, lambda w_=which: [launch(sets[i % len(sets)], bole, w_)
-                                              for i in range(n_in)])
+        n_in = 4 * S
+        calls = launches(which, n_in)
+        g = capture(torch, lambda c_=calls: [c() for c in c_])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     conv_ms, conv_bytes, conv_commit_ms = time_tree_conv(cfg, sets, torch, bole, dev, K)
     d16_ms, d16_bytes, d16_depth = time_depth16(cfg, torch, TreeRound, bole, dev, K)
@@ -958,16 +1268,28 @@ def main():
         assert s_.rnd.error_bits() == 0, "device error bits set"
     dominant, bytes_fn = DOMINANT[args.path]
 
-    nodes = sum(s.forest.N for s in sets) / len(sets)
+    # per step of the timed sequence: set i % S (the mix when K % S != 0)
+    mix = [i % S for i in range(graph_steps(K))]
+    nodes = float(np.mean([sets[j].forest.N for j in mix]))
     value = nodes * cfg.H / (ms_step * 1e-3)
+    tv_bytes = float(np.mean([tree_verify_algorithmic_bytes(sets[j].sizes, cfg.H, cfg.d_k, cfg.d_v,
+                                                            e) for j in mix]))
     if args.path == "deferred":
-        vbytes = np.mean([commit_tree_verify_algorithmic_bytes(s.sizes, s.prev.forest, cfg.H,
-                                                               cfg.d_k, cfg.d_v, e) for s in sets])
+        # each launch commits its own batch's previous round
+        vbytes = float(np.mean([commit_tree_verify_algorithmic_bytes(
+            sets[j].sizes, sets[j].forest, cfg.H, cfg.d_k, cfg.d_v, e) for j in mix]))
     else:
-        vbytes = np.mean([bytes_fn(s.sizes, cfg.H, cfg.d_k, cfg.d_v, e) for s in sets])
-    achieved = vbytes / (avg[dominant] * 1e-3) / 1e9
+        vbytes = float(np.mean([bytes_fn(sets[j].sizes, cfg.H, cfg.d_k, cfg.d_v, e) for j in mix]))
+    # the kernel's duration per launch in a stream of back-to-back launches
+    # (for the deferred path, the timed step's single launch)
+    ms_dom = ms_launch
+    dom_timing = ("marginal time per launch between captured graphs of 128 and 64 back-to-back "
+                  "launches, each replayed 8 times (HIP events; the GPU's start of each replay "
+                  "cancels)")
+    achieved = vbytes / (ms_dom * 1e-3) / 1e9
+    tv_achieved = tv_bytes / (ms_tree_verify * 1e-3) / 1e9
     # a plain copy over the same footprint as the rotated input sets
-    copy_gbs = copy_bandwidth(torch, dev, int(vbytes * len(sets)), 20)
+    copy_gbs = copy_bandwidth(torch, dev, int(vbytes * S), 20)
     # the committed counter record is the default path's dominant kernel
     traffic = traffic_from_profile(kernel_source_hash()) if args.path == "deferred" else None
 
@@ -988,12 +1310,14 @@ def main():
             "workload": f"{cfg.name}: B={cfg.B} trees x T={cfg.T} nodes (random recursive, "
                         f"depth<={cfg.D}), H={cfg.H}, d_k=d_v={cfg.d_k}, {cfg.dtype} q/k/v, "
                         f"f32 gates and state; step = {' + '.join(STEPS[args.path])}"
-                        + (" (this round's verify with the previous round's accepted-path "
-                           "commit inside: one commit and one verify per step)"
+                        + (" (this round's verify with the same requests' previous round's "
+                           "accepted-path commit inside: one commit and one verify per step)"
                            if args.path == "deferred" else ""),
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
-            "nodes": nodes, "input_sets": len(sets), "path": args.path,
-            "timing": "HIP graph replays: 16 captured steps per graph; kernels: 16 launches per graph",
+            "nodes": nodes, "input_sets": S, "path": args.path,
+            "timing": f"{K} back-to-back steps as {K // graph_steps(K)} replay(s) of a captured "
+                      f"graph of {graph_steps(K)} steps, after untimed pre-roll replays; input "
+                      f"sets rotated; per-kernel figures from graphs of {4 * S} launches",
             "ms_per_step_other_path": ms_other,
             "ms_per_step_eager_launches": ms_eager,
             "kernel_ms_back_to_back": avg,
@@ -1028,10 +1352,27 @@ def main():
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": vbytes,
+            "ms_per_launch": ms_dom,
+            "timing": dom_timing,
             "copy_GBs": copy_gbs,
             "frac_of_copy": achieved / copy_gbs,
         },
+        "roofline_tree_verify": {
+            "note": "the verify alone (bole_tree_verify: preparation, factors, solve and "
+                    "readout of one layer, no commit)",
+            "kernel": "bole_tree_verify",
+            "bound": "hbm",
+            "ms": ms_tree_verify,
+            "achieved": tv_achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": tv_achieved / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": tv_bytes,
+            "timing": "as the roofline's dominant kernel",
+        },
     }
+    if not args.no_multilayer:
+        out["multilayer"] = multilayer_record(torch, TreeRound, bole, dev, K)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, 0, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -26,3 +26,29 @@ def test_help_lists_paths_and_workloads():
     assert r.returncode == 0
     for word in ("deferred", "tree", "fused", "split_neumann", "split_inverse", "multilayer"):
         assert word in r.stdout, word
+
+
+def test_deferred_schedule_is_a_real_round_sequence():
+    """Each input set's rounds in a captured graph form a cycle (the graph is
+    replayed): every launch reads the output group its set's previous round
+    wrote, and never the group it writes itself."""
+    import bench
+    for S in (1, 2, 3, 4, 5):
+        for R in range(2 * S, 6 * S + 3):
+            sched = bench.deferred_schedule(R, S)
+            assert [j for j, _, _ in sched] == [i % S for i in range(R)]
+            for j in range(S):
+                rounds = [(c, p) for jj, c, p in sched if jj == j]
+                n = len(rounds)
+                assert n >= 2
+                for m, (c, p) in enumerate(rounds):
+                    assert c != p
+                    assert p == rounds[(m - 1) % n][0]
+                    assert 0 <= c < bench.InputSet.GROUPS
+
+
+def test_graph_steps_divides_k():
+    import bench
+    for k in (1, 20, 1000, 2048, 2049, 4000, 4099):
+        r = bench.graph_steps(k)
+        assert k % r == 0 and r <= max(k, 1) and (r == k or r <= 2048)
