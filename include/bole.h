@@ -140,9 +140,7 @@ BOLE_API int bole_factor_gc(int32_t dtype, const void* q, const void* k, const f
  * 16-row tiles, each diagonal block inverted by its own Neumann series), and
  * reads out O^(r) = B0 + C U.
  * All products run on bf16 MFMA with float32 accumulation; float32 operands
- * (states, G, C, U, and float32 q/k) are split into bf16 hi+lo parts, except
- * that with bf16 q/k/v the two products only O depends on (Q S_pre and C U)
- * use the hi parts: O is stored in bf16.
+ * (states, G, C, U, and float32 q/k) are split into bf16 hi+lo parts.
  *
  *  in   q, k [N,H,d_k], v [N,H,d_v]   dtype
  *  in   logP[N,H], beta[N,H]          float32

@@ -24,9 +24,8 @@
 //  Solve    U_t = (I + G_tt)^-1 (R_t - sum_{s<t} G_ts U_s), tile by tile, with
 //           a permuted K order (load_tri_blocks) that makes the lane's own U
 //           tiles the B operand: U never leaves registers.
-//  Readout  O = B0 + C U, float32 accumulation.  Products that U and the
-//           committed state depend on split every float32 operand hi + lo; O's
-//           own (Q S_pre, C U) do so only for float32 tokens (kOExact).
+//  Readout  O = B0 + C U, float32 accumulation.  Every product splits its
+//           float32 operands hi + lo, O's own (Q S_pre, C U) included.
 //  Stores   U (compact, float32) and O (token dtype) pass through LDS tiles and
 //           leave as 4-element pieces of the nodes' rows; V arrives the same
 //           way, as 16-byte row pieces staged for the accumulator layout.
@@ -85,12 +84,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   static_assert(!(FUSED && SOLVE == kSolveInverse), "W and M come from bole_factor_inverse");
   static_assert(!COMMIT || (FUSED && PREP && SOLVE == kSolveBlocked), "commit inside tree verify");
   static_assert(!EARLY || (DT == BOLE_BF16 && SOLVE == kSolveBlocked), "early tail: bf16, blocked");
-  // O's own products (Q S_pre for B0, C U) carry the split low halves only for
-  // float32 tokens; with bf16 tokens O is stored in bf16, and each product is
-  // taken at that precision (hi parts: relative error near 2^-8, inside the
-  // 2e-2 bar with a 2.5x margin).  Everything U and the committed state depend
-  // on keeps the split products.
-  constexpr bool kOExact = DT == BOLE_F32;
   __shared__ __align__(16) __bf16 stage[SC::NMAT * kMaxTree * SC::LROW];
   // planes: -G hi, -G lo, C hi, C lo
   __shared__ __align__(16) __bf16 gcs[4 * kGcPlane];
@@ -638,11 +631,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
           const int ro = row * SC::LROW + 8 * swz<DT>(row, 4 * kk + g4);
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(stage + ro);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(stage + kMaxTree * SC::LROW + ro);
-          // kOExact: B0 = D_P Q S feeds only O; with bf16 tokens O is stored in
-          // bf16 and S's low half is left out of Q S (K S, which feeds U and
-          // the committed state, keeps it)
+          // B0 = D_P Q S feeds only O, and keeps S's low half all the same:
+          // taken on the hi parts only, O's own products lose about 2^-9 of
+          // each term, and where B0 and C U nearly cancel (beta near 1, q
+          // close to k, a state large against v) that is no longer small
+          // against O (the 2e-2 bar was missed with states 100x the spread
+          // of prefix-built ones)
           qs[mt] = mfma_bf16(aq, b_hi, qs[mt]);
-          if (kOExact) qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
+          qs[mt] = mfma_bf16(aq, b_lo, qs[mt]);
           ks[mt] = mfma_bf16(ak, b_hi, ks[mt]);
           ks[mt] = mfma_bf16(ak, b_lo, ks[mt]);
           if (DT == BOLE_F32) {
@@ -829,11 +825,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
           y = mfma_bf16(wl, rh[J], y);
           y = mfma_bf16(wh, rl[J], y);
           acc = mfma_bf16(mh, rh[J], acc);
-          if (kOExact) {
-            const bf16x8 ml = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
-            acc = mfma_bf16(ml, rh[J], acc);
-            acc = mfma_bf16(mh, rl[J], acc);
-          }
+          const bf16x8 ml = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
+          acc = mfma_bf16(ml, rh[J], acc);
+          acc = mfma_bf16(mh, rl[J], acc);
         }
       }
       u[I] = y;
@@ -852,12 +846,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       for (int J = 0; J <= I / 2; ++J) {
         const int o = gc_frag(16 * I + l16, J, g4);
         const bf16x8 ch = *reinterpret_cast<const bf16x8*>(gcs + 2 * kGcPlane + o);
+        const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
         acc = mfma_bf16(ch, uh[J], acc);
-        if (kOExact) {  // bf16 tokens: C U at the precision O is stored in
-          const bf16x8 cl = *reinterpret_cast<const bf16x8*>(gcs + 3 * kGcPlane + o);
-          acc = mfma_bf16(cl, uh[J], acc);
-          acc = mfma_bf16(ch, ul[J], acc);
-        }
+        acc = mfma_bf16(cl, uh[J], acc);
+        acc = mfma_bf16(ch, ul[J], acc);
       }
       qs[I] = acc;
     }
