@@ -929,50 +929,24 @@ int launch_verify_t(const void* q, const void* k, const void* v, const float* lo
   // would wait at its barrier) reads V as 8-byte pieces of four columns
   constexpr bool kMayEarly = DT == BOLE_BF16 && SOLVE == bole::kSolveBlocked && FUSED;
   const bool early = kMayEarly && d_v % 4 == 0 && (uintptr_t)v % 8 == 0;
-  // A grid larger than one round of resident workgroups (two per CU) runs as
-  // request chunks of at most one round each, back to back on the stream: the
-  // workgroups of a chunk start together and move through their phases in
-  // step, where a second residency round inside one launch starts piecemeal
-  // as first-round workgroups finish.  Each chunk sees the per-request arrays
-  // from its first request on.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    cus = 1 << 20;  // unknown: one launch
-  const int64_t per_req = (int64_t)H * NV;
-  const int64_t cap = 2 * (int64_t)cus;
-  const int max_req = (int)std::max<int64_t>(1, cap / per_req);
-  const int chunks = (B + max_req - 1) / max_req;
-  const int per_chunk = (B + chunks - 1) / chunks;
-  for (int b0 = 0; b0 < B; b0 += per_chunk) {
-    const int Bc = std::min(per_chunk, B - b0);
-    const int64_t gc = (int64_t)b0 * H * bole::kMaxTree * bole::kMaxTree;
-    bole::PrepIO pr = prep;
-    if (pr.tree_depth) pr.tree_depth += b0;
-    bole::CommitIO cc = cm;
-    if (cc.accept) cc.accept += b0;
-    if (cc.tree_off) cc.tree_off += b0;
-    const dim3 grid(Bc * H * NV);
-    const int32_t* slot_c = slot + b0;
-    const int32_t* off_c = tree_off + b0;
-    const int32_t* td_c = tree_depth ? tree_depth + b0 : nullptr;
-    const float* G_c = G ? G + gc : nullptr;
-    const float* C_c = C ? C + gc : nullptr;
-    if (early) {
-      if constexpr (kMayEarly)
-        hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT, true>), grid,
-                           block, 0, s, q, k, v, logP, beta, state_pool, n_slots, slot_c, G_c,
-                           C_c, anc, order, depth, off_c, td_c, Bc, N, H, d_k, d_v, O, U, vecf, pr,
-                           err, cc);
-    } else {
-      hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT>), grid, block, 0,
-                         s, q, k, v, logP, beta, state_pool, n_slots, slot_c, G_c, C_c, anc, order,
-                         depth, off_c, td_c, Bc, N, H, d_k, d_v, O, U, vecf, pr, err, cc);
-    }
-    if (hipGetLastError() != hipSuccess) return BOLE_E_HIP;
+  // One launch whatever the grid: a grid beyond one residency round (two
+  // workgroups per CU) starts its later workgroups as earlier ones finish, so
+  // their loads overlap the earlier ones' tails and stores.  (Split into
+  // back-to-back launches of one round each, 32 requests x 32 heads measured
+  // about 10% slower.)
+  const dim3 grid(B * H * NV);
+  if (early) {
+    if constexpr (kMayEarly)
+      hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT, true>), grid,
+                         block, 0, s, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, anc,
+                         order, depth, tree_off, tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep,
+                         err, cm);
+  } else {
+    hipLaunchKernelGGL((bole::verify_kernel<DT, FUSED, ONE, PREP, SOLVE, COMMIT>), grid, block, 0,
+                       s, q, k, v, logP, beta, state_pool, n_slots, slot, G, C, anc, order, depth,
+                       tree_off, tree_depth, B, N, H, d_k, d_v, O, U, vecf, prep, err, cm);
   }
-  return BOLE_OK;
+  return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 
 template <bool FUSED, int SOLVE = bole::kSolveBlocked>
