@@ -23,45 +23,52 @@ namespace bole {
 constexpr int kMaxConv = 8;        // widest convolution supported
 constexpr int kConvThreads = 256;
 
-template <int DT>
+template <int DT, int WD = kMaxConv>
 struct ConvCfg {
   using Elem = std::conditional_t<DT == BOLE_BF16, uint16_t, float>;
   static constexpr int EPP = 16 / sizeof(Elem);              // elements per 16-byte piece
   static constexpr int CH = DT == BOLE_BF16 ? 256 : 128;      // channels per workgroup (512 B)
   static constexpr int GROUPS = CH / EPP;                    // pieces per row
-  static constexpr int NQ = 2;                               // parts taken in turn
+  static constexpr int NQ = 1;                               // parts taken in turn
   static constexpr int HG = GROUPS / NQ;                     // pieces per row and part
   static constexpr int NODE_LANES = kConvThreads / HG;       // nodes computed at once
   // 16-byte pieces per thread and part: tree rows plus committed state rows
-  static constexpr int PIECES = (kMaxTree + kMaxConv - 1) * HG / kConvThreads + 1;
+  static constexpr int PIECES = (kMaxTree + WD - 1) * HG / kConvThreads + 1;
 };
 
 __device__ __forceinline__ float elem_to_float(uint16_t b) { return bf16_bits_to_float(b); }
 __device__ __forceinline__ float elem_to_float(float f) { return f; }
 
 // grid (B, ceil(C / CH)).  Rows 0..T-1 of the LDS tile hold the tree's inputs
-// for the workgroup's channels, rows kMaxTree .. kMaxTree + W - 2 the committed
-// conv state.  src[i][j] is the tile row of the j-th most recent entry of node
-// i's window (j = 0: node i itself).
+// for the workgroup's channels, rows kMaxTree .. kMaxTree + WD - 2 the
+// committed conv state.  src[i][j] is the tile row of the j-th most recent entry
+// of node i's window (j = 0: node i itself).
 //
-// The workgroup's channels are taken in NQ parts.  A part's loads go out once
-// the part before it has arrived, and the part before it is then computed and
-// stored while they are in flight: the output writes of one part overlap the
-// input reads of the next.  (Issued all at once, every part would arrive only
-// near the end of the whole transfer: the memory system serves the requests
-// of all workgroups interleaved.)
-template <int DT>
+// The width WD is a compile-time constant (the host picks the instantiation):
+// a thread holds exactly WD taps per channel in registers, and the tile has
+// exactly WD - 1 state rows, so narrow convolutions keep more workgroups
+// resident.
+//
+// The workgroup's channels can be taken in NQ parts: a part's loads go out
+// once the part before it has arrived, and the part before it is then computed
+// and stored while they are in flight, so the output writes of one part
+// overlap the input reads of the next.  With the width a compile-time constant
+// (111 registers at W = 4 in bf16, against 159 for a kernel holding every
+// width), one part measures faster at the target (13.2-13.7 us against
+// 13.9-14.1 us for two), so NQ = 1: every load goes out at once.
+template <int DT, int WD>
 __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
     const void* __restrict__ x, const float* __restrict__ weight, const float* __restrict__ bias,
     const void* __restrict__ conv_state, int32_t n_slots, const int32_t* __restrict__ slot,
     const int32_t* __restrict__ parent, const int32_t* __restrict__ tree_off, int32_t N, int32_t C,
-    int32_t Wd, void* __restrict__ y, uint32_t* __restrict__ err) {
-  using CC = ConvCfg<DT>;
+    void* __restrict__ y, uint32_t* __restrict__ err) {
+  using CC = ConvCfg<DT, WD>;
   using Elem = typename CC::Elem;
-  __shared__ __align__(16) Elem tile[kMaxTree + kMaxConv - 1][CC::CH];
-  __shared__ float ws[kMaxConv][CC::CH];
+  constexpr int Wd = WD;
+  __shared__ __align__(16) Elem tile[kMaxTree + WD - 1][CC::CH];
+  __shared__ float ws[WD][CC::CH];
   __shared__ float bs[CC::CH];
-  __shared__ int8_t src[kMaxTree][kMaxConv];
+  __shared__ int8_t src[kMaxTree][WD];
   __shared__ int tree_ok;
 
   const int b = blockIdx.x;
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
     }
   };
   issue(std::integral_constant<int, 0>{});
-  constexpr int kWPer = kMaxConv * CC::CH / kConvThreads;
+  constexpr int kWPer = (WD * CC::CH + kConvThreads - 1) / kConvThreads;
   float wv[kWPer];
 #pragma unroll
   for (int k = 0; k < kWPer; ++k) {
@@ -152,16 +159,15 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
 #pragma unroll
   for (int k = 0; k < kWPer; ++k) {
     const int id = threadIdx.x + kConvThreads * k;
-    ws[id / CC::CH][id - (id / CC::CH) * CC::CH] = wv[k];
+    if (id < WD * CC::CH) ws[id / CC::CH][id - (id / CC::CH) * CC::CH] = wv[k];
   }
   if (threadIdx.x < CC::CH) bs[threadIdx.x] = c0 + (int)threadIdx.x < C ? bv : 0.0f;
   __syncthreads();  // part 0, taps, bias and the window table visible
   if (!tree_ok) return;  // uniform
 
   const int pc = threadIdx.x % CC::HG, nl = threadIdx.x / CC::HG;
-  auto half = [&](auto h_tag, auto wd_tag) {
+  auto half = [&](auto h_tag) {
     constexpr int h = decltype(h_tag)::value;
-    constexpr int WD = decltype(wd_tag)::value;
     const int cl = CC::EPP * (CC::HG * h + pc), c = c0 + cl;
     if (c >= C) return;
     Elem* ye = reinterpret_cast<Elem*>(y) + c;
@@ -202,18 +208,7 @@ __global__ __launch_bounds__(kConvThreads) void tree_conv_kernel(
       __builtin_nontemporal_store(out, reinterpret_cast<u16x8*>(ye + (int64_t)(off + i) * C));
     }
   };
-  auto compute = [&](auto h_tag) {  // the width as a compile-time constant
-    switch (Wd) {
-      case 1: half(h_tag, std::integral_constant<int, 1>{}); break;
-      case 2: half(h_tag, std::integral_constant<int, 2>{}); break;
-      case 3: half(h_tag, std::integral_constant<int, 3>{}); break;
-      case 4: half(h_tag, std::integral_constant<int, 4>{}); break;
-      case 5: half(h_tag, std::integral_constant<int, 5>{}); break;
-      case 6: half(h_tag, std::integral_constant<int, 6>{}); break;
-      case 7: half(h_tag, std::integral_constant<int, 7>{}); break;
-      default: half(h_tag, std::integral_constant<int, 8>{}); break;
-    }
-  };
+  auto compute = [&](auto h_tag) { half(h_tag); };
   auto stage = [&](auto h_tag, auto self) {
     constexpr int h = decltype(h_tag)::value;
     if constexpr (h + 1 < CC::NQ) {
@@ -307,15 +302,29 @@ extern "C" int bole_tree_conv_launch(int32_t dtype, const void* x, const float* 
                                      const int32_t* tree_off, int32_t B, int32_t N, int32_t C,
                                      int32_t W, void* y, uint32_t* err, hipStream_t s) {
   const dim3 block(bole::kConvThreads);
-  if (dtype == BOLE_BF16) {
-    const dim3 grid(B, (C + bole::ConvCfg<BOLE_BF16>::CH - 1) / bole::ConvCfg<BOLE_BF16>::CH);
-    hipLaunchKernelGGL(bole::tree_conv_kernel<BOLE_BF16>, grid, block, 0, s, x, weight, bias,
-                       conv_state, n_slots, slot, parent, tree_off, N, C, W, y, err);
-  } else {
-    const dim3 grid(B, (C + bole::ConvCfg<BOLE_F32>::CH - 1) / bole::ConvCfg<BOLE_F32>::CH);
-    hipLaunchKernelGGL(bole::tree_conv_kernel<BOLE_F32>, grid, block, 0, s, x, weight, bias,
-                       conv_state, n_slots, slot, parent, tree_off, N, C, W, y, err);
-  }
+  auto go = [&](auto dt_tag, auto w_tag) {
+    constexpr int DT = decltype(dt_tag)::value, WD = decltype(w_tag)::value;
+    using CC = bole::ConvCfg<DT, WD>;
+    const dim3 grid(B, (C + CC::CH - 1) / CC::CH);
+    hipLaunchKernelGGL((bole::tree_conv_kernel<DT, WD>), grid, block, 0, s, x, weight, bias,
+                       conv_state, n_slots, slot, parent, tree_off, N, C, y, err);
+  };
+  auto by_width = [&](auto dt_tag) {
+    switch (W) {  // 1 .. kMaxConv, checked by the caller
+      case 1: go(dt_tag, std::integral_constant<int, 1>{}); break;
+      case 2: go(dt_tag, std::integral_constant<int, 2>{}); break;
+      case 3: go(dt_tag, std::integral_constant<int, 3>{}); break;
+      case 4: go(dt_tag, std::integral_constant<int, 4>{}); break;
+      case 5: go(dt_tag, std::integral_constant<int, 5>{}); break;
+      case 6: go(dt_tag, std::integral_constant<int, 6>{}); break;
+      case 7: go(dt_tag, std::integral_constant<int, 7>{}); break;
+      default: go(dt_tag, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  if (dtype == BOLE_BF16)
+    by_width(std::integral_constant<int, BOLE_BF16>{});
+  else
+    by_width(std::integral_constant<int, BOLE_F32>{});
   return hipGetLastError() == hipSuccess ? BOLE_OK : BOLE_E_HIP;
 }
 
