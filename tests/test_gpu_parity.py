@@ -254,6 +254,42 @@ def test_sibling_independence():
     assert not np.array_equal(res[0][1][o + victim], res[1][1][o + victim])
 
 
+@pytest.mark.parametrize("dtype,d_k", [("bf16", 128), ("f32", 64)])
+def test_value_tiles_are_independent(dtype, d_k):
+    """Value tiling changes only the schedule (arXiv page, section IV-B: each
+    value tile's B0, R, U and O need no other tile).  At d_v = 256 every head
+    runs as two 128-column tiles in separate workgroups; each tile's O and U
+    columns must equal, bit for bit, a d_v = 128 call on just those V columns
+    and state rows.  Through bole_tree_verify and through the two-call path
+    (bole_factor_gc + bole_verify)."""
+    from linear_attention_tree_amd import TreeRound
+    from helpers import to_dev
+    cfg = W.Config(f"tiles_{dtype}", 41, B=3, H=2, d_k=d_k, d_v=256, dtype=dtype, tree="fixed",
+                   T=64, D=12, prefix=32)
+    case = make_case(cfg, n_layers=1, seed=6)
+    f = case.forest
+    say(f"invariants: value tiles {dtype} d_k={d_k}")
+    d = to_dev(case, 0)
+    slot = torch.from_numpy(case.slot).cuda()
+    pool = torch.from_numpy(case.S_pre[0]).cuda()  # [slots, H, d_v, d_k]: row v holds S[:, v]
+
+    def run(v, pl):
+        rnd = TreeRound(f.parent, f.tree_off, cfg.H)
+        O_t, U_t, _ = rnd.tree_layer(d["q"], d["k"], v, d["g"], d["beta"], pl, slot)
+        logP = rnd.prep(d["g"][None])[0]
+        O_s, U_s = rnd.layer(d["q"], d["k"], v, logP, d["beta"], pl, slot)
+        torch.cuda.synchronize()
+        assert rnd.error_bits() == 0
+        return [x.clone() for x in (O_t, U_t, O_s, U_s)]
+
+    whole = run(d["v"], pool)
+    for r in range(2):
+        cols = slice(128 * r, 128 * (r + 1))
+        part = run(d["v"][..., cols].contiguous(), pool[:, :, cols, :].contiguous())
+        for w_, p_ in zip(whole, part):
+            assert torch.equal(w_[..., cols], p_)
+
+
 def test_bad_slot_and_accept_bits():
     from linear_attention_tree_amd import TreeRound
     from helpers import to_dev
