@@ -8,8 +8,10 @@ factors and verify with the previous round's commit inside); --path tree
 times bole_tree_verify + bole_commit_path, and --path fused and --path split
 the three- and four-launch forms.  Default workload: 16 requests,
 64-node random trees (depth <= 12), 32 state heads, d_k = d_v = 128, bf16
-q/k/v with float32 gates and states.  Several independent input sets are
-rotated so the bytes touched per rotation exceed the 256 MB last-level cache.
+q/k/v with float32 gates and states.  Eight independent input sets are
+rotated by default, so one rotation touches about 960 MB, several times the
+256 MB last-level cache (with four sets, 480 MB, the default step measured
+about 20% faster: partly served from that cache).
 
 Prints one JSON line.  `value` = tree nodes x heads verified per second.
 """
@@ -59,6 +61,13 @@ def tree_verify_algorithmic_bytes(sizes, H, d_k, d_v, e):
         sum(T * (4 * H + 4 + 16) + 4 for T in sizes))
 
 
+def tree_verify_written_bytes(sizes, H, d_k, d_v, e):
+    """The written part of bole_tree_verify's algorithmic bytes: O and U per
+    node and head, logP per node and head, depth, anc and order per node,
+    tree_depth per tree (the rest is read)."""
+    return int(sum(T * (H * (e * d_v + 4 * d_v) + 4 * H + 16) + 4 for T in sizes))
+
+
 def path_lengths(forest):
     """Nodes on each request's accepted path (root to accepted node), for the
     requests that accept one."""
@@ -81,6 +90,37 @@ def commit_tree_verify_algorithmic_bytes(sizes, prev_forest, H, d_k, d_v, e):
     extra = sum(H * (4 * d_k * d_v + la * (e * d_k + 4 * d_v + 4)) + 8
                 for la in path_lengths(prev_forest))
     return tree_verify_algorithmic_bytes(sizes, H, d_k, d_v, e) + int(extra) + 12 * len(sizes)
+
+
+def commit_tree_verify_written_bytes(sizes, prev_forest, H, d_k, d_v, e):
+    """The written part of bole_commit_tree_verify's algorithmic bytes:
+    bole_tree_verify's, plus every committed slot."""
+    return tree_verify_written_bytes(sizes, H, d_k, d_v, e) + \
+        H * 4 * d_k * d_v * len(path_lengths(prev_forest))
+
+
+def stream_ceiling(torch, dev, read_bytes, write_bytes, n_sets):
+    """GB/s of the baselines library's streaming kernel moving read_bytes in
+    and write_bytes out per launch over n_sets rotated buffer pairs (the
+    footprint and read:write mix of the kernel it is set against): the best of
+    three launch shapes, each timed as the marginal time per back-to-back
+    launch."""
+    from linear_attention_tree_amd import baselines
+    nr, nw = int(read_bytes) // 16, int(write_bytes) // 16
+    src = torch.ones(n_sets * nr * 4, dtype=torch.float32, device=dev)
+    dst = torch.empty(n_sets * nw * 4, dtype=torch.float32, device=dev)
+    best = 0.0
+    for grid, block in ((1024, 256), (2048, 256), (4096, 256)):
+        def calls(n):
+            return [lambda i=i: baselines.stream_mix(src[(i % n_sets) * nr * 4:],
+                                                     dst[(i % n_sets) * nw * 4:], nr, nw,
+                                                     grid, block)
+                    for i in range(n)]
+        ms = marginal_ms(torch, calls, max(64, 2 * n_sets))
+        best = max(best, (nr + nw) * 16 / (ms * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
 
 
 DOMINANT = {  # path -> (launch name, algorithmic bytes of one launch)
@@ -131,7 +171,7 @@ def _short(name):
     return name.split("(")[0].replace("void ", "")
 
 
-def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
+def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write, n_sets):
     """Scaled HBM bytes per dispatch of every library kernel in the two counter
     passes, beside the algorithmic bytes where a model exists (target shape)."""
     def means(d, counter):
@@ -142,7 +182,7 @@ def all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write):
         return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
     fe, wr = means(fetch_dir, "FETCH_SIZE"), means(write_dir, "WRITE_SIZE")
     cfg = W.CONFIGS["target"]
-    forests = [W.make_forest(cfg, seed) for seed in range(4)]
+    forests = [W.make_forest(cfg, seed) for seed in range(n_sets)]
     algo = {
         "bole::" + DOMINANT_KERNEL: np.mean(
             [commit_tree_verify_algorithmic_bytes(f.sizes(), f, cfg.H, cfg.d_k, cfg.d_v, 2)
@@ -180,7 +220,8 @@ def summarize_mfma(mfma_dir, trace_dir, command):
                 float(r["Counter_Value"]))
     dur = {_short(r["Name"]): float(r["AverageNs"]) for r in _csv_rows(trace_dir, "kernel_stats.csv")}
     lines = ["# MFMA, LDS and L2 counters, target workload (rocprofv3 --pmc)", "", "Command:", "", "```",
-             command, "```", "",
+             command, "```", "", "Summarized from its output (durations from the kernel trace) by:",
+             "", "```", summarizer_command(), "```", "",
              "Per dispatch, averaged over the run. bf16 MFMA rate = 512 x "
              "SQ_INSTS_VALU_MFMA_MOPS_BF16 / the kernel's average duration in the kernel trace, "
              f"against the {PEAK_BF16_TFLOPS:.0f} TFLOP/s dense bf16 peak. LDS bank-conflict share = "
@@ -203,46 +244,110 @@ def summarize_mfma(mfma_dir, trace_dir, command):
     print("\n".join(lines))
 
 
-def timed_window(trace_dir, kernel):
-    """Durations (ns) of `kernel`'s dispatches in the timed region of a kernel
-    trace: the first stretch between two consecutive spin-kernel dispatches
-    that holds that kernel's dispatches and nothing else (the bench puts a
-    spin before and after its timed replays).  None when there is none."""
+def marked_windows(trace_dir, kernel):
+    """The stretches of a kernel trace between two consecutive marker
+    dispatches (torch's sleep kernel, named spin_kernel) that hold `kernel`'s
+    dispatches and nothing else, in order: each a list of (start, end)
+    timestamps in ns.  The bench marks its timed K steps first, then the two
+    regions of the dominant kernel's marginal time (graphs of 128 and of 64
+    launches, 8 replays each)."""
     rows = sorted(_csv_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
-    spins = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
-    for a, b in zip(spins, spins[1:]):
+    marks = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
+    out = []
+    for a, b in zip(marks, marks[1:]):
         win = rows[a + 1:b]
         if win and all(kernel in r["Kernel_Name"] for r in win):
-            return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in win]
-    return None
+            out.append([(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in win])
+    return out
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
+def timed_window(trace_dir, kernel):
+    """Durations (ns) of `kernel`'s dispatches in the first marked window (the
+    timed K steps), or None."""
+    w = marked_windows(trace_dir, kernel)
+    return [e - s for s, e in w[0]] if w else None
+
+
+def trace_marginal_us(windows, r=64, replays=8):
+    """The marginal time per launch from a trace's own timestamps: the span of
+    the window of 2r x replays dispatches minus that of r x replays, over
+    r x replays (each span holds `replays` replay starts, which cancel).
+    None without both windows."""
+    spans = {}
+    for w in windows:
+        spans.setdefault(len(w), (w[-1][1] - w[0][0]) / 1e3)
+    if 2 * r * replays not in spans or r * replays not in spans:
+        return None
+    return (spans[2 * r * replays] - spans[r * replays]) / (r * replays)
+
+
+def summarizer_command():
+    """This script's command line as invoked, without the (long) recorded
+    profiling commands."""
+    out, skip = ["python3", "bench.py"], False
+    for a in sys.argv[1:]:
+        if skip:
+            skip = False
+        elif a == "--profile-commands":
+            skip = True
+        elif not a.startswith("--profile-commands="):
+            out.append(a)
+    return " ".join(out)
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands, n_sets,
+                       bench_line=None):
     """Turn three rocprofv3 runs of this script (a kernel trace, a FETCH_SIZE
     pass and a WRITE_SIZE pass, the counter passes preceded by a plain copy of
-    calib_mib MiB) into the text summaries under profiles/ and the counter
-    record the bench line reads its `traffic` from."""
+    calib_mib MiB, all three over the same n_sets rotated input sets) into the
+    text summaries under profiles/ and the counter record the bench line reads
+    its `traffic` from."""
     os.makedirs(PROFILES, exist_ok=True)
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     cfg = W.CONFIGS["target"]
-    forests = [W.make_forest(cfg, seed) for seed in range(4)]
+    forests = [W.make_forest(cfg, seed) for seed in range(n_sets)]
     # the default step's launches each commit their own batch's previous round
     algo = float(np.mean([commit_tree_verify_algorithmic_bytes(f.sizes(), f, cfg.H, cfg.d_k,
                                                                cfg.d_v, 2) for f in forests]))
     lines = ["# Kernel durations, target workload (rocprofv3 --kernel-trace --stats)", "",
-             "Command:", "", "```", commands["trace"], "```", ""]
-    win = timed_window(trace_dir, DOMINANT_KERNEL)
-    if win:
-        w = np.array(win, np.float64) / 1e3
+             "Command:", "", "```", commands["trace"], "```", "",
+             "Summarized from its output by:", "", "```", summarizer_command(), "```", ""]
+    wins = marked_windows(trace_dir, DOMINANT_KERNEL)
+    if wins:
+        w = np.array([e - s for s, e in wins[0]], np.float64) / 1e3
+        span = (wins[0][-1][1] - wins[0][0][0]) / 1e3 / len(w)
         lines += ["## The timed region", "",
-                  "Dispatches of `bole_commit_tree_verify` between the two spin-kernel markers "
+                  "Dispatches of `bole_commit_tree_verify` between the two marker kernels "
                   "the bench launches around its timed replays (the K steps its JSON line "
                   "reports):", "",
-                  "| dispatches | mean us | median us | min us | max us | algorithmic MB | "
-                  "GB/s at the mean | of 8 TB/s |", "|---|---|---|---|---|---|---|---|",
+                  "| dispatches | mean us | median us | min us | max us | span / K us | "
+                  "algorithmic MB | GB/s at the mean | of 8 TB/s |",
+                  "|---|---|---|---|---|---|---|---|---|",
                   f"| {len(w)} | {w.mean():.2f} | {np.median(w):.2f} | {w.min():.2f} | "
-                  f"{w.max():.2f} | {algo / 1e6:.1f} | {algo / (w.mean() * 1e3):.0f} | "
+                  f"{w.max():.2f} | {span:.2f} | {algo / 1e6:.1f} | {algo / (w.mean() * 1e3):.0f} | "
                   f"{algo / (w.mean() * 1e3) / PEAK_HBM_GBS:.3f} |", ""]
+        m = trace_marginal_us(wins)
+        if m is not None:
+            lines += ["## The roofline's duration", "",
+                      "`roofline.ms_per_launch` is a marginal time: graphs of 128 and of 64 "
+                      "back-to-back launches, 8 replays each, each region between marker "
+                      "kernels. From this trace's own timestamps, (span of the 1 024 dispatches "
+                      "- span of the 512) / 512:", "",
+                      "| marginal us per launch | algorithmic MB | GB/s | of 8 TB/s |",
+                      "|---|---|---|---|",
+                      f"| {m:.2f} | {algo / 1e6:.1f} | {algo / (m * 1e3):.0f} | "
+                      f"{algo / (m * 1e3) / PEAK_HBM_GBS:.3f} |", "",
+                      ]
+            if bench_line:
+                d = json.load(open(bench_line))
+                ro = d["roofline"]
+                lines += ["The JSON line the traced run printed, timed with HIP events over the "
+                          "same dispatches:", "",
+                          "| ms_per_step | roofline.ms_per_launch | roofline.frac | "
+                          "frac from the trace's marginal | ratio |", "|---|---|---|---|---|",
+                          f"| {d['ms_per_step'] * 1e3:.2f} us | {ro['ms_per_launch'] * 1e3:.2f} us | "
+                          f"{ro['frac']:.4f} | {algo / (m * 1e3) / PEAK_HBM_GBS:.4f} | "
+                          f"{ro['frac'] / (algo / (m * 1e3) / PEAK_HBM_GBS):.3f} |", ""]
     lines += ["## Every dispatch of the run (warm-up, captures and other paths included)", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
@@ -254,12 +359,16 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
         fh.write("\n".join(lines) + "\n")
 
     def per_dispatch(d, counter):
-        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        rows = sorted((r for r in _csv_rows(d, "counter_collection.csv")
+                       if r["Counter_Name"] == counter), key=lambda r: int(r["Dispatch_Id"]))
         dom = [float(r["Counter_Value"]) for r in rows if DOMINANT_KERNEL in r["Kernel_Name"]]
-        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # the calibration copies run before any library kernel (later copies,
+        # such as the bench's own bandwidth figure, have other sizes)
+        first = next((i for i, r in enumerate(rows) if "bole::" in r["Kernel_Name"]), len(rows))
+        copies = [float(r["Counter_Value"]) for r in rows[:first] if "copyBuffer" in r["Kernel_Name"]]
         if not dom or not copies:
             raise SystemExit(f"{counter}: dominant kernel or calibration copy missing in {d}")
-        return sum(dom) / len(dom), len(dom), max(copies)
+        return sum(dom) / len(dom), len(dom), float(np.median(copies))
 
     fetch, n_f, copy_fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
     write, n_w, copy_write = per_dispatch(write_dir, "WRITE_SIZE")
@@ -279,6 +388,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
           "Commands (one counter per pass; each pass first copies "
           f"{calib_mib} MiB device-to-device for the calibration):", "", "```",
           commands["fetch"], commands["write"], "```", "",
+          "Summarized from their output by:", "", "```", summarizer_command(), "```", "",
           "| quantity | value |", "|---|---|",
           f"| FETCH_SIZE per dispatch (KiB) | {fetch:.0f} over {n_f} dispatches |",
           f"| WRITE_SIZE per dispatch (KiB) | {write:.0f} over {n_w} dispatches |",
@@ -290,7 +400,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calib_mib, commands):
           f"| ratio | {traffic / algo:.3f} |", "",
           f"Kernel source hash: `{rec['kernel_source_hash']}` ({', '.join(KERNEL_SOURCE_NAMES)}); "
           "bench.py reports `traffic` only while it matches.", ""]
-    md += all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write)
+    md += all_kernel_traffic(fetch_dir, write_dir, f_fetch, f_write, n_sets)
     with open(os.path.join(PROFILES, "bole_commit_tree_verify_target_counters.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(rec))
@@ -511,10 +621,62 @@ def graph_steps(k, cap=2048):
     return next(r for r in range(cap, 0, -1) if k % r == 0)
 
 
-# Spin kernel ahead of each timed region (torch.cuda._sleep cycles, about a
-# millisecond): long enough for the host to enqueue the timed replays before the
-# GPU reaches them.
-SPIN_COVER_CYCLES = 2_000_000
+def input_sets(sets, steps, path):
+    """Rotated input sets a run of `steps` steps uses: `sets`, or fewer for the
+    deferred step, whose captured graph must give each set at least two rounds
+    (each set's rounds form a cycle)."""
+    if path != "deferred":
+        return sets
+    r = graph_steps(steps)
+    if r < 4:
+        raise SystemExit(f"the deferred step needs a graph of at least 4 steps; "
+                         f"--steps {steps} gives {r}")
+    return min(sets, r // 2)
+
+
+# A short kernel (torch.cuda._sleep cycles) before and after a timed region:
+# markers that delimit its dispatches in a kernel trace.
+MARKER_CYCLES = 1000
+
+
+def graph_ms(torch, g, r, replays, marker=False):
+    """ms per step of `replays` back-to-back replays of the captured graph g
+    of r steps.  Untimed pre-roll replays (at least 200 steps) are enqueued
+    right before the timed ones with no wait between: the GPU is still busy
+    with them while the host enqueues the timed replays, so the timed region
+    holds no host launch time, only the GPU's own start of each replay, and it
+    opens on a GPU already at full load.  marker: short kernels right before
+    and after the timed replays delimit them in a kernel trace."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for _ in range(max(1, -(-200 // r))):
+        g.replay()
+    if marker:
+        torch.cuda._sleep(MARKER_CYCLES)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    if marker:
+        torch.cuda._sleep(MARKER_CYCLES)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * r)
+
+
+def marginal_ms(torch, calls, r=64, replays=8, marker=False):
+    """Marginal ms per launch of back-to-back launches: the difference between
+    captured graphs of 2r and r launches (calls(n) gives n zero-argument
+    launch calls), each replayed `replays` times after the pre-roll.  The
+    GPU's start of each replay cancels, so this is the kernel's own duration
+    in a stream of launches, the figure a kernel trace reports per dispatch.
+    marker: each of the two timed regions is delimited by marker kernels, so
+    a kernel trace can give the same figure from its own timestamps (the
+    2r-launch region first)."""
+    def one(n):
+        cs = calls(n)
+        return graph_ms(torch, capture(torch, lambda: [c() for c in cs]), n, replays, marker) * n
+    return (one(2 * r) - one(r)) / r
 
 
 def time_steps_eager(sets, bole, path, K, torch):
@@ -554,16 +716,25 @@ def check_graph_replay(s, graph, bole, path, torch):
 
 
 def cpu_model():
-    """The host CPU's model name as /proc/cpuinfo gives it."""
+    """The host CPU's model name as /proc/cpuinfo gives it, with its family and
+    model numbers (a virtualised host may give only a generic name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block
+                key, _, val = line.partition(":")
+                info.setdefault(key.strip(), val.strip())
     except OSError:
         pass
-    import platform
-    return platform.processor() or "unknown"
+    name = info.get("model name")
+    if not name:
+        import platform
+        return platform.processor() or "unknown"
+    if "cpu family" in info and "model" in info:
+        name += f" (family {info['cpu family']}, model {info['model']})"
+    return name
 
 
 def cpu_baseline(cfg, seed, budget_s=12.0):
@@ -605,6 +776,11 @@ def conv_algorithmic_bytes(N, B, C, Wd, e):
     return N * C * e * 2 + B * (Wd - 1) * C * e + C * (Wd + 1) * 4
 
 
+# bytes a timed rotation of inputs touches at least: several times the 256 MB
+# last-level cache
+ROTATION_BYTES = 1 << 30
+
+
 def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     """The first-stage tree convolution at the workload's shape: C = H (2 d_k +
     d_v) channels (the mixed q, k, v projection), width W.CONV_WIDTH.  Returns
@@ -613,8 +789,14 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
+    e = 2 if cfg.dtype == "bf16" else 4
+    nbytes = np.mean([conv_algorithmic_bytes(s_.forest.N, s_.forest.B, C, Wd, e) for s_ in sets])
+    # inputs and outputs of their own, rotated over at least ROTATION_BYTES so
+    # that the last-level cache serves none of them
+    n_in = max(4 * len(sets), -(-ROTATION_BYTES // int(nbytes)))
     runs = []
-    for s_ in sets:
+    for k in range(n_in):
+        s_ = sets[k % len(sets)]
         t = s_.rnd.topo
         N, B = s_.forest.N, s_.forest.B
         x = torch.randn(N, C, generator=gen, device=dev).to(tdt)
@@ -623,13 +805,11 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
         bias = 0.1 * torch.randn(C, generator=gen, device=dev)
         runs.append((x, wgt, bias, st, s_.slot, t.parent, t.tree_off, torch.empty_like(x),
                      s_.rnd.err))
-    n_in = 4 * len(sets)
-    g = capture(torch, lambda: [bole.bole_tree_conv(*runs[i % len(runs)]) for i in range(n_in)])
+    g = capture(torch, lambda: [bole.bole_tree_conv(*runs[i]) for i in range(n_in)])
     ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
-    e = 2 if cfg.dtype == "bf16" else 4
-    nbytes = np.mean([conv_algorithmic_bytes(s_.forest.N, s_.forest.B, C, Wd, e) for s_ in sets])
     # the conv-state commit of the accepted paths (moves W - 1 rows per request)
-    commits = [(r[3], r[4], r[0], r[5], r[6], s_.accept, r[8]) for r, s_ in zip(runs, sets)]
+    commits = [(r[3], r[4], r[0], r[5], r[6], sets[k % len(sets)].accept, r[8])
+               for k, r in enumerate(runs)]
     gc = capture(torch, lambda: [bole.bole_conv_commit(*commits[i % len(commits)])
                                  for i in range(n_in)])
     ms_commit = time_graphs([gc], max(reps // n_in, 5), torch) / n_in
@@ -652,15 +832,20 @@ def time_depth16(cfg, torch, TreeRound, bole, dev, reps):
     under a depth cap of 16 instead of cfg.D (ms per launch, algorithmic bytes)."""
     from dataclasses import replace
     c16 = replace(cfg, D=16)
-    sets = [InputSet(c16, seed, torch, TreeRound, dev) for seed in range(2)]
+    e = 2 if cfg.dtype == "bf16" else 4
+    probe = InputSet(c16, 0, torch, TreeRound, dev)
+    nb0 = tree_verify_algorithmic_bytes(probe.sizes, cfg.H, cfg.d_k, cfg.d_v, e)
+    # enough sets that a rotation touches ROTATION_BYTES
+    n_sets = max(2, -(-ROTATION_BYTES // int(nb0)))
+    sets = [probe] + [InputSet(c16, seed, torch, TreeRound, dev) for seed in range(1, n_sets)]
     for s_ in sets:
         run_step(s_, bole, "tree")
-    n_in = 16
-    g = capture(torch, lambda: [launch(sets[i % 2], bole, "tree_verify") for i in range(n_in)])
+    n_in = 2 * n_sets
+    g = capture(torch, lambda: [launch(sets[i % n_sets], bole, "tree_verify") for i in range(n_in)])
     ms = time_graphs([g], max(reps // n_in, 5), torch) / n_in
     depth = max(int(s_.rnd.topo.tree_depth.max().item()) for s_ in sets)
-    nb = np.mean([tree_verify_algorithmic_bytes(s_.sizes, cfg.H, cfg.d_k, cfg.d_v,
-                                                2 if cfg.dtype == "bf16" else 4) for s_ in sets])
+    nb = np.mean([tree_verify_algorithmic_bytes(s_.sizes, cfg.H, cfg.d_k, cfg.d_v, e)
+                  for s_ in sets])
     return ms, nb, depth
 
 
@@ -782,6 +967,54 @@ def time_bucketed_rounds(cfg, x, pool, slot, torch, dev, K):
             "deferred_by_capacity": out_d}
 
 
+def workload_record(cname, torch, TreeRound, bole, dev):
+    """One layer of another of the pages' workload shapes: the marginal time per
+    launch of bole_commit_tree_verify (the default step's kernel) and of
+    bole_tree_verify, over enough rotated input sets that a rotation touches
+    ROTATION_BYTES."""
+    cfg = W.CONFIGS[cname]
+    e = 2 if cfg.dtype == "bf16" else 4
+    probe = InputSet(cfg, 0, torch, TreeRound, dev)
+    b0 = commit_tree_verify_algorithmic_bytes(probe.sizes, probe.forest, cfg.H, cfg.d_k, cfg.d_v, e)
+    n = max(2, -(-ROTATION_BYTES // int(b0)))
+    sets = [probe] + [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(1, n)]
+    for s_ in sets:
+        s_.fill_groups(bole)
+
+    def deferred(r):
+        return [lambda j=j, c=c, pv=pv: launch(sets[j], bole, "commit_tree_verify", c, pv)
+                for j, c, pv in deferred_schedule(r, n)]
+
+    def tree(r):
+        return [lambda i=i: launch(sets[i % n], bole, "tree_verify") for i in range(r)]
+
+    r = max(64, 2 * n)
+    ms_c = marginal_ms(torch, deferred, r)
+    ms_t = marginal_ms(torch, tree, r)
+    for s_ in sets:
+        assert s_.rnd.error_bits() == 0, "device error bits set"
+    nodes = float(np.mean([s_.forest.N for s_ in sets]))
+    bc = float(np.mean([commit_tree_verify_algorithmic_bytes(s_.sizes, s_.forest, cfg.H, cfg.d_k,
+                                                              cfg.d_v, e) for s_ in sets]))
+    bt = float(np.mean([tree_verify_algorithmic_bytes(s_.sizes, cfg.H, cfg.d_k, cfg.d_v, e)
+                        for s_ in sets]))
+
+    def rec(ms, nb):
+        return {"us_per_launch": ms * 1e3, "algorithmic_MB": nb / 1e6,
+                "frac_of_hbm_peak": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "node_heads_per_s": nodes * cfg.H / (ms * 1e-3)}
+
+    out = {"workload": f"{cfg.name}: B={cfg.B} trees ({cfg.tree}, up to {cfg.T} nodes, depth<="
+                       f"{cfg.D}), H={cfg.H}, d_k=d_v={cfg.d_k}, {cfg.dtype} q/k/v, one layer",
+           "nodes": nodes, "input_sets": n, "rotation_MB": round(bc * n / 1e6, 1),
+           "timing": "marginal time per launch between captured graphs of 2r and r back-to-back "
+                     f"launches (r = {r}), 8 replays each",
+           "bole_commit_tree_verify": rec(ms_c, bc), "bole_tree_verify": rec(ms_t, bt)}
+    del sets, probe
+    torch.cuda.empty_cache()
+    return out
+
+
 def multilayer_record(torch, TreeRound, bole, dev, reps):
     """The multi-layer round at its full shape (36 layers, 32 trees x 64 nodes,
     32 heads, d = 128, bf16; token operands and states drawn on the device)
@@ -835,14 +1068,15 @@ def multilayer_record(torch, TreeRound, bole, dev, reps):
         bole.bole_commit_path(pool, slot, x.k, U, lp, topo[1], t.tree_off, accept, rnd.err)
 
     def timed(fn, n_rep):
-        """ms per replay of fn's captured graph: pre-roll replays, then a busy
-        spin while the host enqueues the timed replays."""
+        """ms per replay of fn's captured graph: two pre-roll replays (whole
+        rounds, milliseconds of GPU work) enqueued right before the timed ones
+        keep the GPU busy while the host enqueues those."""
         g = capture(torch, fn)
+        torch.cuda.synchronize()
         for _ in range(2):
             g.replay()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(SPIN_COVER_CYCLES)
         e0.record()
         for _ in range(n_rep):
             g.replay()
@@ -1111,7 +1345,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="target", choices=sorted(W.CONFIGS))
-    ap.add_argument("--sets", type=int, default=4, help="rotated independent input sets")
+    ap.add_argument("--sets", type=int, default=8,
+                    help="rotated independent input sets (fewer when the deferred step's "
+                         "graph of --steps steps cannot give each set two rounds)")
     ap.add_argument("--path", default="deferred", choices=sorted(STEPS),
                     help="deferred: commit_tree_verify (the previous round's commit inside this "
                          "round's verify); tree: tree_verify + commit; "
@@ -1119,6 +1355,8 @@ def main():
                          "split: the four calls; split_neumann, split_inverse: the four calls "
                          "with the other exact solves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="leave out the one-layer records of the batched and ragged workloads")
     ap.add_argument("--no-multilayer", action="store_true",
                     help="leave out the 36-layer round and its per-node snapshot baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -1129,6 +1367,8 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from three rocprofv3 runs of this script "
                          "(no GPU needed)")
+    ap.add_argument("--trace-bench-line", default=None,
+                    help="with --summarize-profiles: the JSON line the traced run printed")
     ap.add_argument("--profile-commands", default="",
                     help="JSON {trace, fetch, write} of the commands that made the runs")
     args = ap.parse_args()
@@ -1136,9 +1376,11 @@ def main():
         summarize_mfma(*args.summarize_mfma, args.profile_commands or "?")
         return
     if args.summarize_profiles:
+        # the runs' --steps / --sets / --path give the sets they rotated
         summarize_profiles(*args.summarize_profiles, args.calibrate_copy_mib or 256,
                            json.loads(args.profile_commands or "{}") or
-                           {"trace": "?", "fetch": "?", "write": "?"})
+                           {"trace": "?", "fetch": "?", "write": "?"},
+                           input_sets(args.sets, args.steps, args.path), args.trace_bench_line)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -1163,7 +1405,8 @@ def main():
         del src, dst
     if args.sets < 2:
         raise SystemExit("--sets must be at least 2 (a step commits the previous set's round)")
-    sets = [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(args.sets)]
+    n_sets = input_sets(args.sets, args.steps, args.path)
+    sets = [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(n_sets)]
     S = len(sets)
     e = 2 if cfg.dtype == "bf16" else 4
     for s_ in sets:
@@ -1197,26 +1440,7 @@ def main():
         return [lambda i=i: launch(sets[i % S], bole, which) for i in range(r)]
 
     def time_graph(g, r, replays, marker=False):
-        """ms per step of `replays` back-to-back replays of the captured graph
-        g of r steps, after untimed pre-roll replays.  A long spin kernel ahead
-        of the first timed replay keeps the GPU busy while the host enqueues
-        the timed replays, so the timed region holds no host launch time; it
-        only holds the GPU's own start of each replay.  marker: the spin and a
-        short one after the timed replays delimit them in a kernel trace."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        for _ in range(max(1, -(-200 // r))):
-            g.replay()
-        torch.cuda._sleep(SPIN_COVER_CYCLES)
-        e0.record()
-        for _ in range(replays):
-            g.replay()
-        e1.record()
-        if marker:
-            torch.cuda._sleep(1000)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (replays * r)
+        return graph_ms(torch, g, r, replays, marker)
 
     def capture_steps(which, r):
         calls = launches(which, r)
@@ -1228,22 +1452,16 @@ def main():
         r = graph_steps(k)
         return time_graph(capture_steps(which, r), r, k // r, marker)
 
-    def time_per_launch(which, r=64, replays=8):
-        """Marginal ms per launch of back-to-back launches: the difference
-        between graphs of 2r and r launches, each replayed `replays` times
-        after the busy spin.  The GPU's start of each replay cancels, so this
-        is the kernel's own duration in a stream of launches, the figure a
-        kernel trace reports per dispatch."""
-        t1 = time_graph(capture_steps(which, r), r, replays) * r
-        t2 = time_graph(capture_steps(which, 2 * r), 2 * r, replays) * 2 * r
-        return (t2 - t1) / r
+    def time_per_launch(which, r=64, replays=8, marker=False):
+        return marginal_ms(torch, lambda n: launches(which, n), r, replays, marker)
 
-    torch.cuda._sleep(1)  # load the spin kernel before the timed regions
+    torch.cuda._sleep(1)  # load the marker kernel before the timed regions
     ms_step = time_k(args.path, K, marker=True)
     # the dominant kernel's own duration per launch (the step's one launch
     # for the deferred path), and the verify kernel alone (the step's verify
     # without the commit), each as the marginal time per back-to-back launch
-    ms_launch = time_per_launch(args.path if args.path == "deferred" else DOMINANT[args.path][0])
+    ms_launch = time_per_launch(args.path if args.path == "deferred" else DOMINANT[args.path][0],
+                                marker=True)
     ms_tree_verify = time_per_launch("tree_verify")
     ms_other = {p: time_k(p, max(K // 2, 2 * S)) for p in STEPS if p != args.path}
     ms_eager = time_steps_eager(sets, bole, args.path, max(K // 2, 10), torch)
@@ -1290,6 +1508,16 @@ def main():
     tv_achieved = tv_bytes / (ms_tree_verify * 1e-3) / 1e9
     # a plain copy over the same footprint as the rotated input sets
     copy_gbs = copy_bandwidth(torch, dev, int(vbytes * S), 20)
+    # the streaming kernel at each verify kernel's footprint and read:write mix
+    tv_written = float(np.mean([tree_verify_written_bytes(sets[j].sizes, cfg.H, cfg.d_k, cfg.d_v,
+                                                          e) for j in mix]))
+    if args.path == "deferred":
+        dom_written = float(np.mean([commit_tree_verify_written_bytes(
+            sets[j].sizes, sets[j].forest, cfg.H, cfg.d_k, cfg.d_v, e) for j in mix]))
+        ceil_dom = stream_ceiling(torch, dev, vbytes - dom_written, dom_written, S)
+    else:
+        ceil_dom = None
+    ceil_tv = stream_ceiling(torch, dev, tv_bytes - tv_written, tv_written, S)
     # the committed counter record is the default path's dominant kernel
     traffic = traffic_from_profile(kernel_source_hash()) if args.path == "deferred" else None
 
@@ -1314,7 +1542,8 @@ def main():
                            "accepted-path commit inside: one commit and one verify per step)"
                            if args.path == "deferred" else ""),
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
-            "nodes": nodes, "input_sets": S, "path": args.path,
+            "nodes": nodes, "input_sets": S,
+            "rotation_MB": round(vbytes * S / 1e6, 1), "path": args.path,
             "timing": f"{K} back-to-back steps as {K // graph_steps(K)} replay(s) of a captured "
                       f"graph of {graph_steps(K)} steps, after untimed pre-roll replays; input "
                       f"sets rotated; per-kernel figures from graphs of {4 * S} launches",
@@ -1356,6 +1585,11 @@ def main():
             "timing": dom_timing,
             "copy_GBs": copy_gbs,
             "frac_of_copy": achieved / copy_gbs,
+            "stream_ceiling": None if ceil_dom is None else {
+                "note": "a plain streaming kernel (baselines/stream.hip) moving the same read and "
+                        "written bytes per launch over the same rotated footprint",
+                "written_bytes_per_launch": dom_written, "GBs": ceil_dom,
+                "frac_of_peak": ceil_dom / PEAK_HBM_GBS, "kernel_frac_of_ceiling": achieved / ceil_dom},
         },
         "roofline_tree_verify": {
             "note": "the verify alone (bole_tree_verify: preparation, factors, solve and "
@@ -1369,10 +1603,16 @@ def main():
             "frac": tv_achieved / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": tv_bytes,
             "timing": "as the roofline's dominant kernel",
+            "stream_ceiling": {
+                "written_bytes_per_launch": tv_written, "GBs": ceil_tv,
+                "frac_of_peak": ceil_tv / PEAK_HBM_GBS, "kernel_frac_of_ceiling": tv_achieved / ceil_tv},
         },
     }
+    if not args.no_workloads:
+        out["config"]["other_workloads"] = {c: workload_record(c, torch, TreeRound, bole, dev)
+                                            for c in ("batched", "ragged")}
     if not args.no_multilayer:
-        out["multilayer"] = multilayer_record(torch, TreeRound, bole, dev, K)
+        out["config"]["multilayer"] = multilayer_record(torch, TreeRound, bole, dev, K)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, 0, args.cpu_budget)
     print(json.dumps(out), flush=True)

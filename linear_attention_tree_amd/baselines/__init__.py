@@ -4,7 +4,9 @@ comparison with SGLang-Tree's serial delta-rule verifier).  Not part of
 libbole's interface: the benchmark runs it in the same harness as the
 closed-form path, and the tests check it against the oracle.
 
-Its kernels are in snapshot.hip, built into libbole_baselines.so beside it.
+Its kernels are in snapshot.hip, built into libbole_baselines.so beside it,
+with stream.hip's plain streaming kernel, the bandwidth ceiling the verify
+kernels are set against.
 The per-round level lists (nodes grouped by depth, with global parent
 indices) are the baseline's own host-side preparation, done once per round.
 """
@@ -35,6 +37,8 @@ def lib() -> ctypes.CDLL:
                                      i32, P]
         L.snapshot_commit.restype = ctypes.c_int
         L.snapshot_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P]
+        L.stream_mix.restype = ctypes.c_int
+        L.stream_mix.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, i32, i32, P]
         _lib = L
     return _lib
 
@@ -45,6 +49,18 @@ def _ptr(t):
 
 def _stream(stream):
     return ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+
+
+def stream_mix(src, dst, n_read, n_write, grid=2048, block=256, stream=None):
+    """One launch of the streaming kernel: n_read 16-byte vectors read from the
+    device tensor src, n_write written to dst (grid-stride, non-temporal
+    writes)."""
+    if n_read * 16 > src.numel() * src.element_size() or \
+            n_write * 16 > dst.numel() * dst.element_size():
+        raise ValueError("stream_mix: counts exceed the buffers")
+    code = lib().stream_mix(_ptr(src), _ptr(dst), n_read, n_write, grid, block, _stream(stream))
+    if code != 0:
+        raise RuntimeError(f"stream_mix failed: {code}")
 
 
 def level_lists(parent, tree_off):

@@ -33,3 +33,22 @@ def test_level_lists_refuse_bad_topology(parent):
     from linear_attention_tree_amd.baselines import level_lists
     with pytest.raises(ValueError):
         level_lists(np.array(parent), np.array([0, 3]))
+
+
+def test_stream_mix_refuses_bad_arguments():
+    """The streaming kernel's argument checks run before any launch (no GPU
+    needed): negative counts, launch shapes outside 1..65536 workgroups of a
+    multiple of 64 threads up to 1024, and null or misaligned buffers."""
+    from linear_attention_tree_amd.baselines import lib
+    L = lib()
+    buf = (np.zeros(64, np.float32).ctypes.data + 15) // 16 * 16  # 16-byte aligned host address
+    ok = dict(src=buf, dst=buf, n_read=1, n_write=1, grid=1, block=64)
+    bad = [dict(n_read=-1), dict(n_write=-1), dict(grid=0), dict(grid=65537), dict(block=32),
+           dict(block=96), dict(block=2048), dict(src=None), dict(dst=None), dict(src=buf + 4),
+           dict(dst=buf + 8)]
+    for change in bad:
+        a = {**ok, **change}
+        assert L.stream_mix(a["src"], a["dst"], a["n_read"], a["n_write"], a["grid"],
+                            a["block"], None) == 2, change
+    # zero counts need no buffers; they are refused only for a bad launch shape
+    assert L.stream_mix(None, None, 0, 0, 0, 64, None) == 2

@@ -3,7 +3,9 @@ beside the closed-form path) against the float64 oracle: O, U, the committed
 state, and the stored snapshots of chosen nodes (each equals the oracle's
 walked state after that node), on the float32 exactness case, the bf16
 workloads and one layer of the multi-layer round's shape (32 trees x 64 nodes,
-32 heads).  Bars as for the library: 1e-4 for float32 tokens, 2e-2 for bf16."""
+32 heads).  Bars as for the library: 1e-4 for float32 tokens, 2e-2 for bf16.
+Also the streaming kernel the bench sets the verify kernels against: it reads
+and writes every vector it is given."""
 
 import sys
 
@@ -87,3 +89,27 @@ def test_snapshot_verifier_at_multilayer_shape():
                 S_pre=[W.make_states(cfg, n_slots, 0, 0)], slot=slot, n_slots=n_slots)
     say("snapshot verifier: one layer of 32 trees x 64 nodes, 32 heads")
     check(case, "multilayer shape")
+
+
+@pytest.mark.parametrize("n_read,n_write,grid,block", [(1000, 777, 3, 64), (4096, 4096, 8, 256),
+                                                        (0, 100, 2, 128), (50, 0, 1, 64)])
+def test_stream_mix_moves_every_vector(n_read, n_write, grid, block):
+    """Written vector i holds, in components 1..3, the number of source vectors
+    its thread read (a source of ones; thread i mod threads reads the indices
+    congruent to it), and in component 0 that count plus i; nothing past
+    n_write is touched."""
+    from linear_attention_tree_amd.baselines import stream_mix
+    say(f"stream_mix read {n_read} write {n_write} grid {grid} block {block}")
+    src = torch.ones(max(n_read, 1) * 4, dtype=torch.float32, device="cuda")
+    dst = torch.full(((n_write + 8) * 4,), -7.0, dtype=torch.float32, device="cuda")
+    stream_mix(src, dst, n_read, n_write, grid, block)
+    torch.cuda.synchronize()
+    out = dst.view(-1, 4).cpu().numpy()
+    nt = grid * block
+    i = np.arange(n_write)
+    tid = i % nt
+    count = np.where(tid < n_read, (n_read - 1 - tid) // nt + 1, 0).astype(np.float32)
+    assert np.array_equal(out[:n_write, 1], count)
+    assert np.array_equal(out[:n_write, 3], count)
+    assert np.array_equal(out[:n_write, 0], count + i.astype(np.float32))
+    assert np.all(out[n_write:] == -7.0)
