@@ -52,3 +52,46 @@ def test_graph_steps_divides_k():
     for k in (1, 20, 1000, 2048, 2049, 4000, 4099):
         r = bench.graph_steps(k)
         assert k % r == 0 and r <= max(k, 1) and (r == k or r <= 2048)
+
+
+def test_trace_windows_and_marginal(tmp_path):
+    """The profile summary's reading of a kernel trace: the stretches between
+    marker kernels that hold only the dominant kernel, in order, and the
+    marginal time per launch from the 1 024- and 512-dispatch windows' spans
+    (8 replays of 128 and of 64 launches, each replay starting with a gap that
+    the difference cancels)."""
+    import csv
+    import bench
+    K = bench.DOMINANT_KERNEL
+    rows, t = [], 0
+
+    def add(name, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur + 100  # 0.1 us between dispatches
+
+    def region(n_launch, replays, dur_ns, start_gap_ns):
+        nonlocal t
+        add("spin_kernel(long)", 1000)
+        for _ in range(replays):
+            t += start_gap_ns
+            for _ in range(n_launch):
+                add(f"void bole::{K}(args)", dur_ns)
+        add("spin_kernel(long)", 1000)
+
+    add("other_kernel", 5000)
+    region(20, 1, 31000, 9000)        # the timed K steps
+    region(128, 8, 30000, 9000)       # the marginal's two regions
+    region(64, 8, 30000, 9000)
+    add(f"void bole::{K}(args)", 30000)  # outside any window
+    with open(tmp_path / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    wins = bench.marked_windows(str(tmp_path), K)
+    assert [len(x) for x in wins] == [20, 1024, 512]
+    assert bench.timed_window(str(tmp_path), K) == [31000] * 20
+    # per launch: 30 us of kernel plus the 0.1 us between dispatches; the
+    # replay-start gaps (8 in each region) cancel
+    assert abs(bench.trace_marginal_us(wins) - 30.1) < 1e-9
+    assert bench.trace_marginal_us(wins[:2]) is None
