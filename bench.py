@@ -639,18 +639,25 @@ def input_sets(sets, steps, path):
 MARKER_CYCLES = 1000
 
 
+# Untimed steps replayed right before a timed region (tens of milliseconds of
+# GPU work): a region timed straight after host-side setup, with the GPU idle
+# meanwhile, ran about 5% slower over its first few hundred steps.
+PREROLL_STEPS = 2000
+
+
 def graph_ms(torch, g, r, replays, marker=False):
     """ms per step of `replays` back-to-back replays of the captured graph g
-    of r steps.  Untimed pre-roll replays (at least 200 steps) are enqueued
-    right before the timed ones with no wait between: the GPU is still busy
-    with them while the host enqueues the timed replays, so the timed region
-    holds no host launch time, only the GPU's own start of each replay, and it
-    opens on a GPU already at full load.  marker: short kernels right before
-    and after the timed replays delimit them in a kernel trace."""
+    of r steps.  Untimed pre-roll replays (at least PREROLL_STEPS steps) are
+    enqueued right before the timed ones with no wait between: the GPU is
+    still busy with them while the host enqueues the timed replays, so the
+    timed region holds no host launch time, only the GPU's own start of each
+    replay, and it opens on a GPU that has been at full load for a while.
+    marker: short kernels right before and after the timed replays delimit
+    them in a kernel trace."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    for _ in range(max(1, -(-200 // r))):
+    for _ in range(max(1, -(-PREROLL_STEPS // r))):
         g.replay()
     if marker:
         torch.cuda._sleep(MARKER_CYCLES)
