@@ -1347,6 +1347,7 @@ def round_main(cfg, args, torch, TreeRound, bole, dev):
 
 
 def main():
+    global PREROLL_STEPS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
@@ -1361,6 +1362,9 @@ def main():
                          "fused: prep + factor_verify + commit; "
                          "split: the four calls; split_neumann, split_inverse: the four calls "
                          "with the other exact solves")
+    ap.add_argument("--preroll-steps", type=int, default=PREROLL_STEPS,
+                    help="untimed steps replayed ahead of every timed region (a counter pass, "
+                         "which times nothing, can take fewer and dispatch less)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="leave out the one-layer records of the batched and ragged workloads")
@@ -1379,6 +1383,7 @@ def main():
     ap.add_argument("--profile-commands", default="",
                     help="JSON {trace, fetch, write} of the commands that made the runs")
     args = ap.parse_args()
+    PREROLL_STEPS = max(1, args.preroll_steps)
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.profile_commands or "?")
         return

@@ -76,7 +76,7 @@ def conv_cfg(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("Wd", [1, 2, 4, 8])
+@pytest.mark.parametrize("Wd", [1, 2, 3, 4, 5, 6, 7, 8])  # each width is its own instantiation
 def test_tree_conv_parity(dtype, Wd):
     cfg = conv_cfg(dtype)
     forest = W.make_forest(W.CONFIGS["target"], seed=Wd)
