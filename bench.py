@@ -1595,6 +1595,11 @@ def main():
             "algorithmic_bytes_per_launch": vbytes,
             "ms_per_launch": ms_dom,
             "timing": dom_timing,
+            # the same bytes over the K timed steps' own time (for the deferred
+            # path a step is this one launch; the step time also holds the
+            # graph replay's start)
+            "frac_at_step_time": (vbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS
+                                  if args.path == "deferred" else None),
             "copy_GBs": copy_gbs,
             "frac_of_copy": achieved / copy_gbs,
             "stream_ceiling": None if ceil_dom is None else {
