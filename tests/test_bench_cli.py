@@ -95,3 +95,22 @@ def test_trace_windows_and_marginal(tmp_path):
     # replay-start gaps (8 in each region) cancel
     assert abs(bench.trace_marginal_us(wins) - 30.1) < 1e-9
     assert bench.trace_marginal_us(wins[:2]) is None
+
+
+def test_input_sets_rule():
+    """The deferred step's captured graph of K steps must give each rotated
+    set two rounds, so a short run rotates fewer sets; other paths keep them;
+    a graph of fewer than four steps is refused."""
+    import pytest as _pytest
+    import bench
+    assert bench.input_sets(8, 1000, "deferred") == 8
+    assert bench.input_sets(8, 20, "deferred") == 8
+    assert bench.input_sets(8, 10, "deferred") == 5
+    assert bench.input_sets(8, 4, "deferred") == 2
+    assert bench.input_sets(8, 10, "tree") == 8
+    with _pytest.raises(SystemExit):
+        bench.input_sets(8, 3, "deferred")
+    # every accepted combination yields a valid deferred schedule
+    for k in (4, 5, 7, 10, 16, 20, 33, 1000):
+        S = bench.input_sets(8, k, "deferred")
+        bench.deferred_schedule(bench.graph_steps(k), S)
