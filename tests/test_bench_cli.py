@@ -114,3 +114,83 @@ def test_input_sets_rule():
     for k in (4, 5, 7, 10, 16, 20, 33, 1000):
         S = bench.input_sets(8, k, "deferred")
         bench.deferred_schedule(bench.graph_steps(k), S)
+
+
+def test_summarize_profiles_end_to_end(tmp_path, monkeypatch):
+    """--summarize-profiles on synthetic rocprofv3 output: the calibration takes
+    the copies that run before any library kernel (a later, larger copy is
+    ignored), the counters scale by the copy's known size, the record carries
+    the current kernel source hash, and the trace summary gives the marginal
+    time from the marked windows next to the traced run's own line."""
+    import csv
+    import json
+    import bench
+    out = tmp_path / "profiles"
+    out.mkdir()
+    monkeypatch.setattr(bench, "PROFILES", str(out))
+    monkeypatch.setattr(bench, "PROFILE_COUNTERS", str(out / "counters.json"))
+    K = bench.DOMINANT_KERNEL
+    name = f"void bole::{K}(args)"
+
+    def write_csv(path, fields, rows):
+        path.parent.mkdir(parents=True, exist_ok=True)
+        with open(path, "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=fields)
+            w.writeheader()
+            w.writerows(rows)
+
+    # kernel trace: the timed K = 20 steps, then the marginal's 128- and 64-launch regions
+    rows, t = [], 0
+
+    def add(n, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": n, "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur
+
+    for n_launch, replays in ((20, 1), (128, 8), (64, 8)):
+        add("spin_kernel", 500)
+        for _ in range(replays):
+            t += 9000
+            for _ in range(n_launch):
+                add(name, 30000)
+        add("spin_kernel", 500)
+    write_csv(tmp_path / "trace" / "run_kernel_trace.csv",
+              ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    write_csv(tmp_path / "trace" / "run_kernel_stats.csv",
+              ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+              [{"Name": name, "Calls": 1556, "AverageNs": 30000, "MinNs": 30000, "MaxNs": 30000}])
+
+    def counters(counter, copy_kib, dom_kib):
+        rs, i = [], 0
+        for _ in range(3):  # the calibration copies, first in the run
+            rs.append({"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer",
+                       "Counter_Name": counter, "Counter_Value": copy_kib})
+            i += 1
+        for _ in range(5):
+            rs.append({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                       "Counter_Value": dom_kib})
+            i += 1
+        rs.append({"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer",
+                   "Counter_Name": counter, "Counter_Value": 10 * copy_kib})  # the bench's own copy
+        return rs
+
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    write_csv(tmp_path / "fetch" / "run_counter_collection.csv", fields,
+              counters("FETCH_SIZE", 131072, 30000))
+    write_csv(tmp_path / "write" / "run_counter_collection.csv", fields,
+              counters("WRITE_SIZE", 262144, 57000))
+    line = tmp_path / "line.json"
+    line.write_text(json.dumps({"ms_per_step": 0.0305,
+                                "roofline": {"ms_per_launch": 0.030, "frac": 0.4987}}))
+    bench.summarize_profiles(str(tmp_path / "trace"), str(tmp_path / "fetch"),
+                             str(tmp_path / "write"), 256,
+                             {"trace": "T", "fetch": "F", "write": "W"}, 8, str(line))
+    rec = json.load(open(out / "counters.json"))
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == (30000 * 2.0 + 57000 * 1.0) * 1024
+    assert rec["kernel_source_hash"] == bench.kernel_source_hash()
+    assert bench.traffic_from_profile(bench.kernel_source_hash()) == rec["hbm_bytes_per_launch"]
+    md = open(out / "bole_kernels_target_trace.md").read()
+    assert "| 20 | 30.00 | 30.00 |" in md          # the timed window's dispatches
+    assert "| 30.00 |" in md                        # the marginal from the trace
+    assert "0.4987" in md                           # the traced run's own line
