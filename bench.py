@@ -1488,6 +1488,10 @@ def main():
         g = capture(torch, lambda c_=calls: [c() for c in c_])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
     conv_ms, conv_bytes, conv_commit_ms = time_tree_conv(cfg, sets, torch, bole, dev, K)
+    # the streaming kernel with the convolution's bytes: y is the written part
+    conv_written = float(np.mean([s_.forest.N for s_ in sets])) * W.conv_channels(cfg) * e
+    conv_ceil = stream_ceiling(torch, dev, conv_bytes - conv_written, conv_written,
+                               max(2, -(-ROTATION_BYTES // int(conv_bytes))))
     d16_ms, d16_bytes, d16_depth = time_depth16(cfg, torch, TreeRound, bole, dev, K)
     from linear_attention_tree_amd import ForestBuilder
     forest_runs = {}
@@ -1575,6 +1579,10 @@ def main():
                 "achieved_GBs": conv_bytes / (conv_ms * 1e-3) / 1e9,
                 "frac_of_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "algorithmic_bytes_per_launch": conv_bytes,
+                "stream_ceiling": {"written_bytes_per_launch": conv_written, "GBs": conv_ceil,
+                                   "frac_of_peak": conv_ceil / PEAK_HBM_GBS,
+                                   "kernel_frac_of_ceiling":
+                                       conv_bytes / (conv_ms * 1e-3) / 1e9 / conv_ceil},
                 "conv_commit_ms": conv_commit_ms,
             },
             "forest_build": {
