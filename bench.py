@@ -784,8 +784,17 @@ def conv_algorithmic_bytes(N, B, C, Wd, e):
 
 
 # bytes a timed rotation of inputs touches at least: several times the 256 MB
-# last-level cache
+# last-level cache.  The count of rotated inputs is capped: a small workload
+# would otherwise need hundreds of thousands of them (and a captured graph of
+# as many launches); its rotation then stays cache-sized, as its record says.
 ROTATION_BYTES = 1 << 30
+MAX_ROTATED_INPUTS = 64    # per-launch inputs (the convolution, the streaming kernel)
+MAX_ROTATED_SETS = 16      # whole input sets (verify workloads)
+
+
+def rotation_count(nbytes, lo, cap):
+    """Inputs to rotate so that they touch ROTATION_BYTES, between lo and cap."""
+    return int(min(cap, max(lo, -(-ROTATION_BYTES // max(int(nbytes), 1)))))
 
 
 def time_tree_conv(cfg, sets, torch, bole, dev, reps):
@@ -800,7 +809,7 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     nbytes = np.mean([conv_algorithmic_bytes(s_.forest.N, s_.forest.B, C, Wd, e) for s_ in sets])
     # inputs and outputs of their own, rotated over at least ROTATION_BYTES so
     # that the last-level cache serves none of them
-    n_in = max(4 * len(sets), -(-ROTATION_BYTES // int(nbytes)))
+    n_in = rotation_count(nbytes, 4 * len(sets), MAX_ROTATED_INPUTS)
     runs = []
     for k in range(n_in):
         s_ = sets[k % len(sets)]
@@ -820,7 +829,7 @@ def time_tree_conv(cfg, sets, torch, bole, dev, reps):
     gc = capture(torch, lambda: [bole.bole_conv_commit(*commits[i % len(commits)])
                                  for i in range(n_in)])
     ms_commit = time_graphs([gc], max(reps // n_in, 5), torch) / n_in
-    return ms, nbytes, ms_commit
+    return ms, nbytes, ms_commit, n_in
 
 
 def copy_bandwidth(torch, dev, footprint_bytes, reps):
@@ -843,7 +852,7 @@ def time_depth16(cfg, torch, TreeRound, bole, dev, reps):
     probe = InputSet(c16, 0, torch, TreeRound, dev)
     nb0 = tree_verify_algorithmic_bytes(probe.sizes, cfg.H, cfg.d_k, cfg.d_v, e)
     # enough sets that a rotation touches ROTATION_BYTES
-    n_sets = max(2, -(-ROTATION_BYTES // int(nb0)))
+    n_sets = rotation_count(nb0, 2, MAX_ROTATED_SETS)
     sets = [probe] + [InputSet(c16, seed, torch, TreeRound, dev) for seed in range(1, n_sets)]
     for s_ in sets:
         run_step(s_, bole, "tree")
@@ -853,7 +862,7 @@ def time_depth16(cfg, torch, TreeRound, bole, dev, reps):
     depth = max(int(s_.rnd.topo.tree_depth.max().item()) for s_ in sets)
     nb = np.mean([tree_verify_algorithmic_bytes(s_.sizes, cfg.H, cfg.d_k, cfg.d_v, e)
                   for s_ in sets])
-    return ms, nb, depth
+    return ms, nb, depth, n_sets
 
 
 def time_forest_build(cfg, torch, ForestBuilder, dev, reps, capacity):
@@ -983,7 +992,7 @@ def workload_record(cname, torch, TreeRound, bole, dev):
     e = 2 if cfg.dtype == "bf16" else 4
     probe = InputSet(cfg, 0, torch, TreeRound, dev)
     b0 = commit_tree_verify_algorithmic_bytes(probe.sizes, probe.forest, cfg.H, cfg.d_k, cfg.d_v, e)
-    n = max(2, -(-ROTATION_BYTES // int(b0)))
+    n = rotation_count(b0, 2, MAX_ROTATED_SETS)
     sets = [probe] + [InputSet(cfg, seed, torch, TreeRound, dev) for seed in range(1, n)]
     for s_ in sets:
         s_.fill_groups(bole)
@@ -1487,12 +1496,12 @@ def main():
         calls = launches(which, n_in)
         g = capture(torch, lambda c_=calls: [c() for c in c_])
         avg[which] = time_graphs([g], max(K // n_in, 5), torch) / n_in
-    conv_ms, conv_bytes, conv_commit_ms = time_tree_conv(cfg, sets, torch, bole, dev, K)
+    conv_ms, conv_bytes, conv_commit_ms, conv_inputs = time_tree_conv(cfg, sets, torch, bole, dev, K)
     # the streaming kernel with the convolution's bytes: y is the written part
     conv_written = float(np.mean([s_.forest.N for s_ in sets])) * W.conv_channels(cfg) * e
     conv_ceil = stream_ceiling(torch, dev, conv_bytes - conv_written, conv_written,
-                               max(2, -(-ROTATION_BYTES // int(conv_bytes))))
-    d16_ms, d16_bytes, d16_depth = time_depth16(cfg, torch, TreeRound, bole, dev, K)
+                               rotation_count(conv_bytes, 2, MAX_ROTATED_INPUTS))
+    d16_ms, d16_bytes, d16_depth, d16_sets = time_depth16(cfg, torch, TreeRound, bole, dev, K)
     from linear_attention_tree_amd import ForestBuilder
     forest_runs = {}
     for cap in (cfg.B * cfg.T, 768):
@@ -1569,6 +1578,7 @@ def main():
             "tree_verify_depth_cap_16": {
                 "note": "sensitivity: the same shape with trees drawn under a depth cap of 16",
                 "ms": d16_ms, "deepest_tree": d16_depth,
+                "rotation_MB": round(d16_bytes * d16_sets / 1e6, 1),
                 "achieved_GBs": d16_bytes / (d16_ms * 1e-3) / 1e9,
                 "frac_of_hbm_peak": d16_bytes / (d16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             },
@@ -1576,6 +1586,7 @@ def main():
                 "note": "first pipeline stage: the short causal convolution over each node's "
                         "ancestors, with bias and SiLU; not part of the step",
                 "channels": W.conv_channels(cfg), "width": W.CONV_WIDTH, "ms": conv_ms,
+                "rotation_MB": round(conv_bytes * conv_inputs / 1e6, 1),
                 "achieved_GBs": conv_bytes / (conv_ms * 1e-3) / 1e9,
                 "frac_of_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "algorithmic_bytes_per_launch": conv_bytes,
