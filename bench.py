@@ -1568,7 +1568,12 @@ def main():
                            if args.path == "deferred" else ""),
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
             "nodes": nodes, "input_sets": S,
-            "rotation_MB": round(vbytes * S / 1e6, 1), "path": args.path,
+            "rotation_MB": round(vbytes * S / 1e6, 1),
+            "rotation_note": (None if vbytes * S >= 900e6 else
+                              "the rotated inputs touch less than about 900 MB (3.5x the 256 MB "
+                              "last-level cache): part of every figure here is served from that "
+                              "cache (more --sets, or --steps >= 2 x --sets, to avoid it)"),
+            "path": args.path,
             "timing": f"{K} back-to-back steps as {K // graph_steps(K)} replay(s) of a captured "
                       f"graph of {graph_steps(K)} steps, after untimed pre-roll replays; input "
                       f"sets rotated; per-kernel figures from graphs of {4 * S} launches",
