@@ -1569,10 +1569,12 @@ def main():
             "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
             "nodes": nodes, "input_sets": S,
             "rotation_MB": round(vbytes * S / 1e6, 1),
-            "rotation_note": (None if vbytes * S >= 900e6 else
-                              "the rotated inputs touch less than about 900 MB (3.5x the 256 MB "
-                              "last-level cache): part of every figure here is served from that "
-                              "cache (more --sets, or --steps >= 2 x --sets, to avoid it)"),
+            # measured: 480 MB rotated made the default kernel 20% faster than
+            # 957 MB; 673 MB and more measured the same as 1.3 GB
+            "rotation_note": (None if vbytes * S >= 600e6 else
+                              "the rotated inputs touch less than about 600 MB: the figures may "
+                              "be partly served from the 256 MB last-level cache (more --sets, "
+                              "with --steps at least twice --sets, avoid it)"),
             "path": args.path,
             "timing": f"{K} back-to-back steps as {K // graph_steps(K)} replay(s) of a captured "
                       f"graph of {graph_steps(K)} steps, after untimed pre-roll replays; input "
